@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 prefill path on one MI355X.
+
+One step = the W4A4 prefill of the four Qwen3-8B linear layers at 8192 tokens
+(QKV 4096->6144, O 4096->4096, gate_up 4096->24576, down 12288->4096): for
+each layer, the dynamic-alpha activation quantizer (amax pass + quantize
+pass) followed by the NVFP4 GEMM with BF16 output.  Weights are quantized
+once before timing (offline, as in a deployed prefill worker).
+
+The headline value is TFLOP/s including activation quantization:
+sum(2*M*N*K) / (time of the four quantize+GEMM pairs).  Alongside it the
+script times, outside the headline: the in-library BF16 GEMM at the same
+shapes (speedup), the fused quantize-in-GEMM path, the BF16 decode GEMMs at
+batch 1/8/64 on the same weights, and the oracle on the host cores on a
+bounded slice of the same workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4/FP6 MFMA
+F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 MFMA
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "NVFP4 prefill GEMM TFLOPS (incl. act quant), % FP4 MFMA peak, speedup vs BF16"
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_gemm_qwen3_8b_m8192_gate_up_counters.md")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--no-extras", action="store_true", help="only the headline NVFP4 prefill timing")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle leg")
+    return p.parse_args()
+
+
+def _bf16_tensor(bits):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "nvfp4_prefill_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile():
+    """HBM bytes per gate_up GEMM launch from the committed counter summary, if
+    it was taken on the current kernel source (else None)."""
+    try:
+        txt = open(PROFILE_COUNTERS).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in txt.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("gemm_source_sha256_16") != _source_hash("gemm.hip", "nvfp4_device.hpp"):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every entry point is given)."""
+
+    def __init__(self):
+        import torch
+
+        self.torch = torch
+        self.pairs = {}
+
+    def span(self, key):
+        torch = self.torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        self.pairs.setdefault(key, []).append((s, e))
+        return s, e
+
+    def total_ms(self, key):
+        return sum(s.elapsed_time(e) for s, e in self.pairs.get(key, []))
+
+    def count(self, key):
+        return len(self.pairs.get(key, []))
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the NVFP4 prefill path here has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from nvfp4_prefill_gemm_amd import binding as nv
+    from nvfp4_prefill_gemm_amd import workloads as wl
+
+    nv.lib()  # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda", 0)
+    w = wl.WORKLOADS["qwen3_8b_m8192"]
+    M = w.M
+    t_setup = time.time()
+
+    # ---------------------------------------------------------------- inputs
+    layers = []
+    for li, (name, K, N) in enumerate(w.linears):
+        a_bits, w_bits = wl.layer_inputs(w, li)
+        x = _bf16_tensor(a_bits)
+        wb = _bf16_tensor(w_bits)
+        wc, ws, wa = nv.nvfp4_quantize(wb)  # offline weight quantization (untimed)
+        layers.append(dict(
+            name=name, K=K, N=N, x=x, w_bf16=wb, wc=wc, ws=ws, wa=wa,
+            ac=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            asc=torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+            aal=torch.empty(1, dtype=torch.float32, device=dev),
+            ws_buf=torch.empty(max(nv.quantize_workspace_size(M, K), 4), dtype=torch.uint8, device=dev),
+            y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        del a_bits, w_bits
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    flops_step = sum(wl.flops(M, L["N"], L["K"]) for L in layers)
+
+    # ------------------------------------------------------- headline: NVFP4
+    def nvfp4_step(timer=None):
+        for L in layers:
+            if timer:
+                sq, eq = timer.span(("quant", L["name"]))
+                sq.record()
+            nv.nvfp4_quantize(L["x"], L["ac"], L["asc"], L["aal"], workspace=L["ws_buf"])
+            if timer:
+                eq.record()
+                sg, eg = timer.span(("gemm", L["name"]))
+                sg.record()
+            nv.nvfp4_gemm(L["ac"], L["asc"], L["aal"], L["wc"], L["ws"], L["wa"], out=L["y"])
+            if timer:
+                eg.record()
+
+    for _ in range(args.warmup):
+        nvfp4_step()
+    torch.cuda.synchronize()
+    timer = Timer()
+    t0 = time.perf_counter()
+    s_all, e_all = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_all.record()
+    for _ in range(args.steps):
+        nvfp4_step(timer)
+    e_all.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    step_ms = s_all.elapsed_time(e_all) / args.steps
+    per_layer = {}
+    for L in layers:
+        q = timer.total_ms(("quant", L["name"])) / args.steps
+        g = timer.total_ms(("gemm", L["name"])) / args.steps
+        per_layer[L["name"]] = dict(M=M, N=L["N"], K=L["K"], quant_us=round(q * 1e3, 2), gemm_us=round(g * 1e3, 2),
+                                    gemm_tflops=round(wl.flops(M, L["N"], L["K"]) / (g * 1e-3) / 1e12, 1),
+                                    quant_gbps=round(M * L["K"] * 4.5625 / (q * 1e-3) / 1e9, 1))
+    kern_ms = sum(v["quant_us"] + v["gemm_us"] for v in per_layer.values()) / 1e3
+    value = flops_step / (step_ms * 1e-3) / 1e12
+    gemm_ms_total = sum(v["gemm_us"] for v in per_layer.values()) / 1e3
+    quant_ms_total = sum(v["quant_us"] for v in per_layer.values()) / 1e3
+    quant_bytes = sum(M * L["K"] * 4.5625 for L in layers)
+
+    # dominant kernel: the gate_up NVFP4 GEMM launch
+    gu = per_layer["gate_up"]
+    gu_flops = wl.flops(M, gu["N"], gu["K"])
+    gu_tflops = gu_flops / (gu["gemm_us"] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gu_tflops / F16_PEAK_TFLOPS, 4), "traffic": _traffic_from_profile(),
+                "kernel": "gemm_kernel<NVFP4> gate_up 8192x24576x4096 (FP16 MFMA on exact q*sigma)",
+                "frac_of_fp4_peak": round(gu_tflops / FP4_PEAK_TFLOPS, 4)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "linears": [[n, k, nn] for n, k, nn in w.linears],
+                   "activations": "N(0,1) with 0.5% channels x20, BF16", "weights": "N(0,0.02) BF16 -> NVFP4 offline",
+                   "alpha": "dynamic", "out_dtype": "bf16", "storage": "nvfp4 (e2m1 codes + e4m3 per 16 + fp32)"},
+        "frac_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),
+        "frac_f16_mfma_peak": round(value / F16_PEAK_TFLOPS, 4),
+        "gemm_only_tflops": round(flops_step / (gemm_ms_total * 1e-3) / 1e12, 2),
+        "quantizer_gbps": round(quant_bytes / (quant_ms_total * 1e-3) / 1e9, 1),
+        "per_layer": per_layer,
+        "wall_ms_per_step": round(wall_ms / args.steps, 4),
+        "kernel_ms_per_step": round(kern_ms, 4),
+        "roofline": roofline,
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_extras:
+        result.update(extras(args, nv, wl, layers, M, flops_step, step_ms))
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, wl, w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    out = {}
+    reps = max(3, args.steps // 2)
+
+    # BF16 prefill GEMMs at the same shapes (the speedup denominator)
+    def bf16_step():
+        for L in layers:
+            nv.bf16_gemm(L["x"], L["w_bf16"], out=L["y"])
+    for _ in range(2):
+        bf16_step()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        bf16_step()
+    e.record()
+    torch.cuda.synchronize()
+    bf16_ms = s.elapsed_time(e) / reps
+    out["bf16_tflops"] = round(flops_step / (bf16_ms * 1e-3) / 1e12, 2)
+    out["speedup_vs_bf16"] = round(bf16_ms / nvfp4_step_ms, 3)
+
+    # fused quantize-in-GEMM prologue (dynamic alpha: amax pass + fused GEMM)
+    def fused_step():
+        for L in layers:
+            nv.nvfp4_quant_gemm(L["x"], L["wc"], L["ws"], L["wa"], a_alpha=L["aal"], out=L["y"],
+                                workspace=L["ws_buf"])
+    for _ in range(2):
+        fused_step()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fused_step()
+    e.record()
+    torch.cuda.synchronize()
+    fused_ms = s.elapsed_time(e) / reps
+    out["fused_tflops"] = round(flops_step / (fused_ms * 1e-3) / 1e12, 2)
+
+    # BF16 decode GEMMs on the same weights; two rotating weight copies so the
+    # 256 MB Infinity Cache cannot hold a step's weights
+    copies = [[L["w_bf16"] for L in layers], [L["w_bf16"].clone() for L in layers]]
+    decode = {}
+    for Md in wl.PHASE_SPLIT_DECODE_M:
+        xs = [torch.randn((Md, L["K"]), device=dev).to(torch.bfloat16) for L in layers]
+        ys = [torch.empty((Md, L["N"]), dtype=torch.bfloat16, device=dev) for L in layers]
+
+        def dec_step(c):
+            for i, L in enumerate(layers):
+                nv.bf16_gemm(xs[i], copies[c][i], out=ys[i])
+        for c in (0, 1):
+            dec_step(c)
+        torch.cuda.synchronize()
+        n = 10
+        s.record()
+        for r in range(n):
+            dec_step(r & 1)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / n
+        nbytes = sum(2 * L["N"] * L["K"] + 2 * Md * L["K"] + 2 * Md * L["N"] for L in layers)
+        decode[str(Md)] = {"us_per_step": round(ms * 1e3, 1), "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                           "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 3)}
+    out["decode_bf16"] = decode
+    del copies
+    return out
+
+
+def cpu_baseline(args, wl, w):
+    """The oracle (plain C, threads over rows) on the host cores: activation
+    quantization plus exact GEMM for a slab of rows of every layer, scaled to
+    TFLOP/s.  Weights are quantized outside the timed region, as on the GPU."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    wq = []
+    for li, (name, K, N) in enumerate(w.linears):
+        wb = wl.weights(N, K, wl.rng(w.config_id, li, 1))
+        wq.append(oracle.quantize(wb, nthreads=threads))
+
+    # time only quantize + GEMM (input generation excluded)
+    def timed(rows):
+        flops, spent = 0, 0.0
+        for li, (name, K, N) in enumerate(w.linears):
+            a = wl.activations(rows, K, wl.rng(w.config_id, li, 0))
+            ta = time.perf_counter()
+            A = oracle.quantize(a, nthreads=threads)
+            oracle.gemm_exact(*A, *wq[li], nthreads=threads)
+            spent += time.perf_counter() - ta
+            flops += wl.flops(rows, N, K)
+        return flops, spent
+
+    rows = max(threads, 16)
+    flops, spent = timed(rows)
+    if spent < args.cpu_seconds / 4:
+        rows = int(min(w.M, max(rows, rows * args.cpu_seconds / max(spent, 1e-3))))
+        rows = max(threads, (rows // threads) * threads)
+        flops, spent = timed(rows)
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.M} token rows of each of the 4 Qwen3-8B linears: oracle quantize "
+                      f"(dynamic alpha over the slab) + exact int64 GEMM against the full NVFP4 weights; "
+                      f"{spent:.1f} s", "seconds": round(spent, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

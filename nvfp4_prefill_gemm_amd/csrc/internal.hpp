@@ -1,0 +1,46 @@
+// Internal launch interface shared by the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Number of per-workgroup partial maxima the amax pass writes for a tensor.
+int amax_parts(int64_t rows, int64_t cols);
+
+hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                                uint32_t *partials, int nparts, hipStream_t s);
+
+// dynamic != 0: alpha = max(partials[0..nparts)) / 2688 is written to *alpha.
+hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                           uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials,
+                           int nparts, hipStream_t s);
+
+// alpha from partials only (fused path, dynamic mode).
+hipError_t launch_alpha_from_partials(const uint32_t *partials, int nparts, float *alpha, hipStream_t s);
+
+enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
+
+hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                             const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                             int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                             hipStream_t s);
+
+hipError_t launch_gemm_fused(const uint16_t *x, int64_t ld_x, const float *a_alpha,
+                             const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                             int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                             hipStream_t s);
+
+hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                            void *out, int out_type, int64_t ld_out, hipStream_t s);
+
+hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                              void *out, int out_type, int64_t ld_out, hipStream_t s);
+
+// Largest M routed to the skinny decode kernel by bf16_gemm.
+constexpr int64_t kSkinnyMaxM = 64;
+
+hipError_t launch_fill_zero(void *out, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s);
+
+}  // namespace nvfp4

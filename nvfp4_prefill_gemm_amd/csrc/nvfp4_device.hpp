@@ -1,0 +1,109 @@
+// Device-side NVFP4 format helpers for gfx950.
+//
+// NVFP4 (Mix-Quant, Section 3.3): E2M1 element codes, one FP8 E4M3 scale per
+// 16 elements, one FP32 tensor scale.  The rounding here is done with IEEE
+// bit manipulation and compare ladders; every function is round-to-nearest,
+// ties-to-even, on the FP32 value it is given.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// 16-byte streaming load (data read once: non-temporal hint).
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr float kQmax = 6.0f;         // largest finite E2M1 magnitude
+constexpr float kE4M3Max = 448.0f;    // largest finite E4M3 ("FN") value
+constexpr float kAlphaDen = 2688.0f;  // kQmax * kE4M3Max
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// FP32 -> BF16 bits, nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eq. 3's projection onto the E4M3 grid: nearest-even, saturating at 448.
+// s >= 0.  Returns the 8-bit code (sign bit clear).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+    if (!(s < kE4M3Max)) return 0x7Eu;
+    if (s < 0.015625f) {
+        // below the smallest normal 2^-6: the grid is m * 2^-9, m = 0..8, and
+        // code m (m = 8 is the smallest normal, code 0x08).
+        return (uint32_t)__builtin_rintf(s * 512.0f);
+    }
+    uint32_t b = __float_as_uint(s);
+    // keep 3 mantissa bits, nearest-even; a carry moves into the exponent
+    uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+    uint32_t code = r - ((127u - 7u) << 3);  // rebias 127 -> 7
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E4M3 code (sign clear) -> FP32 value, exact.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// Eq. 2's projection onto E2M1: nearest-even with clipping to +-6, sign of v
+// kept (so -0 and tiny negatives give 0x8).  Tie points 0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5 go to the even mantissa.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    float a = __builtin_fabsf(v);
+    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Correctly rounded FP32 division (IEEE), independent of fast-math flags.
+__device__ __forceinline__ float div_rn(float x, float y) { return __fdiv_rn(x, y); }
+
+// One 16-element block: scale code and tensor-scaled divisor, from the block's
+// amax and the tensor scale alpha (Eq. 3).
+struct BlockScale {
+    uint32_t code;  // E4M3 code of sigma_b
+    float sigma;    // sigma_b
+    float d;        // fl32(alpha * sigma_b): the divisor of Eq. 2
+};
+__device__ __forceinline__ BlockScale block_scale(float amax_b, float alpha) {
+    float t = alpha * kQmax;
+    float s = (t > 0.0f) ? div_rn(amax_b, t) : 0.0f;
+    BlockScale r;
+    r.code = e4m3_encode(s);
+    r.sigma = e4m3_decode(r.code);
+    r.d = alpha * r.sigma;
+    return r;
+}
+
+// Eq. 2 for one element: code of x / d, or signed zero when d == 0.
+__device__ __forceinline__ uint32_t quant_elem(float x, float d) {
+    float v = (d > 0.0f) ? div_rn(x, d) : __uint_as_float(__float_as_uint(x) & 0x80000000u);
+    return e2m1_encode(v);
+}
+
+// E2M1 code (4 bits) -> FP16 bits of the value q (exact).
+__device__ __forceinline__ uint32_t e2m1_to_f16_bits(uint32_t c) {
+    uint32_t mag = c & 7u;
+    uint32_t b = mag >= 2u ? (mag + 28u) << 9 : (mag ? 0x3800u : 0u);
+    return b | ((c & 8u) << 12);
+}
+
+// FP32 value of an E4M3 code as FP16 (exact for every finite E4M3 value).
+__device__ __forceinline__ half_t e4m3_to_f16(uint32_t c) { return (half_t)e4m3_decode(c); }
+
+}  // namespace nvfp4

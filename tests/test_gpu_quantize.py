@@ -1,0 +1,148 @@
+"""GPU parity of the NVFP4 quantizer against the oracle: codes, scales and the
+tensor scale must match bit for bit (Mix-Quant Section 3.3, Eq. 2 and Eq. 3)."""
+import numpy as np
+import pytest
+
+from nvfp4_prefill_gemm_amd import workloads as wl
+from tests.gpu_util import bf16_dev, f32_dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from nvfp4_prefill_gemm_amd import binding
+
+    binding.lib()
+    return binding
+
+
+def _gpu_quant(nv, xb, alpha=None, ld=None):
+    import torch
+
+    x = bf16_dev(xb)
+    if ld is not None and ld != xb.shape[1]:
+        big = torch.zeros((xb.shape[0], ld), dtype=torch.bfloat16, device="cuda")
+        big[:, : xb.shape[1]] = x
+        x = big[:, : xb.shape[1]]
+    if alpha is None:
+        c, s, a = nv.nvfp4_quantize(x)
+    else:
+        c, s, a = nv.nvfp4_quantize(x, alpha=f32_dev([alpha]), static_alpha=True)
+    return host(c), host(s), np.float32(host(a)[0])
+
+
+def _assert_same(got, want, what):
+    c, s, a = got
+    wc, ws, wa = want
+    assert a.view(np.uint32) == np.float32(wa).view(np.uint32), f"{what}: alpha {a!r} != {wa!r}"
+    bad = np.argwhere(s != ws)
+    assert bad.size == 0, f"{what}: {len(bad)} scale mismatches, first {bad[:3].tolist()}"
+    bad = np.argwhere(c != wc)
+    assert bad.size == 0, f"{what}: {len(bad)} code-byte mismatches, first {bad[:3].tolist()}"
+
+
+def test_tiny_config_bit_exact(nv, oracle_mod):
+    w = wl.WORKLOADS["tiny"]
+    a, wt = wl.layer_inputs(w, 0)
+    for name, xb in (("A", a), ("W", wt)):
+        say("quantize tiny", name, xb.shape)
+        _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), f"tiny {name}")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (5, 1040), (130, 272), (257, 4096)])
+def test_ragged_shapes(nv, oracle_mod, rows, cols):
+    g = np.random.default_rng(rows * 1000 + cols)
+    xb = wl.to_bf16_bits(g.standard_normal((rows, cols), dtype=np.float32) * 2)
+    say("quantize ragged", rows, cols)
+    _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), f"{rows}x{cols}")
+
+
+def test_static_alpha_and_strided_rows(nv, oracle_mod):
+    g = np.random.default_rng(5)
+    xb = wl.to_bf16_bits(g.standard_t(4.0, size=(64, 512)).astype(np.float32))
+    for alpha in (0.0123, 1.0, 3.0e-6):
+        say("quantize static alpha", alpha)
+        _assert_same(_gpu_quant(nv, xb, alpha=alpha), oracle_mod.quantize(xb, alpha=alpha), f"static {alpha}")
+    say("quantize strided ld=520")
+    _assert_same(_gpu_quant(nv, xb, ld=520), oracle_mod.quantize(xb), "strided")
+
+
+def _special_tensor():
+    """Zero blocks, signed zeros, E2M1 ties, tiny and saturating blocks (alpha = 1)."""
+    rows = []
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    r = np.zeros(64, dtype=np.float32)
+    r[0] = 6.0
+    r[1:8] = ties
+    r[8:15] = -np.array(ties)
+    r[15] = -0.0
+    r[16:32] = 0.0
+    r[20] = -0.0
+    r[32:48] = 2.0 ** -100
+    r[48] = 6144.0
+    r[49] = -6144.0
+    rows.append(r)
+    for amax_b in (6 * 2.0 ** -11, 6 * 2.0 ** -10, 18 * 2.0 ** -11, 6.375, 2640.0, 6144.0):
+        q = np.zeros(64, dtype=np.float32)
+        q[3] = amax_b
+        q[17] = -amax_b / 3
+        q[40] = amax_b * 0.75
+        rows.append(q)
+    return wl.to_bf16_bits(np.stack(rows))
+
+
+def test_special_values(nv, oracle_mod):
+    xb = _special_tensor()
+    say("quantize special values, static alpha 1")
+    _assert_same(_gpu_quant(nv, xb, alpha=1.0), oracle_mod.quantize(xb, alpha=1.0), "special static")
+    say("quantize special values, dynamic")
+    _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), "special dynamic")
+    z = np.zeros((8, 32), dtype=np.uint16)
+    z[3, 5] = 0x8000  # -0.0
+    say("quantize all-zero tensor")
+    _assert_same(_gpu_quant(nv, z), oracle_mod.quantize(z), "all zero")
+
+
+def test_dense_tie_neighbourhood(nv, oracle_mod):
+    """Every BF16 value around each E2M1 tie (times a few scales): the quotient
+    x / (alpha sigma) lands on and next to the tie points."""
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+    base = wl.to_bf16_bits(ties).astype(np.int32)
+    vals = (base[:, None] + np.arange(-6, 7)[None, :]).ravel().astype(np.uint16)
+    rows = []
+    for scale_exp in (0, -3, 5):
+        v = wl.bf16_bits_to_f32(vals) * np.float32(2.0 ** scale_exp)
+        v = np.concatenate([v, -v])
+        pad = (-len(v)) % 15
+        v = np.concatenate([v, np.zeros(pad, dtype=np.float32)]).reshape(-1, 15)
+        blk = np.concatenate([np.full((v.shape[0], 1), 6.0 * 2.0 ** scale_exp, dtype=np.float32), v], axis=1)
+        rows.append(blk.reshape(-1))
+    n = max(len(r) for r in rows)
+    x = np.zeros((len(rows), n), dtype=np.float32)
+    for i, r in enumerate(rows):
+        x[i, : len(r)] = r
+    xb = wl.to_bf16_bits(x)
+    say("quantize tie neighbourhood", xb.shape)
+    _assert_same(_gpu_quant(nv, xb, alpha=1.0), oracle_mod.quantize(xb, alpha=1.0), "ties static")
+    _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), "ties dynamic")
+
+
+@pytest.mark.parametrize("layer", range(4))
+def test_qwen3_8b_m8192_full_tensors(nv, oracle_mod, layer):
+    w = wl.WORKLOADS["qwen3_8b_m8192"]
+    a, wt = wl.layer_inputs(w, layer)
+    for name, xb in (("A", a), ("W", wt)):
+        say("quantize qwen3-8b m8192", w.linears[layer][0], name, xb.shape)
+        _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), f"layer {layer} {name}")
+
+
+def test_student_t_long_prefill_full_tensor(nv, oracle_mod):
+    w = wl.WORKLOADS["qwen3_8b_m32768_t4"]
+    _, K, _ = w.linears[3]
+    xb = wl.activations(w.M, K, wl.rng(w.config_id, 3, 0), w.act_dist)
+    say("quantize student-t m32768 down-proj input", xb.shape)
+    _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), "student-t 32768x12288")
