@@ -14,11 +14,15 @@
 // copied tiles) and the fused path that quantizes BF16 activations in the
 // staging step.
 //
-// Tiling: 128 x 128 output tile per 256-thread workgroup (2 x 2 waves of
-// 64 x 64, each a 2 x 2 grid of 32x32x16 MFMAs), K step 64, LDS double
-// buffer (64 KB).  LDS rows are 64 halves = eight 16-byte chunks; chunk c of
-// row r lives at chunk slot c ^ (r & 7) so the MFMA operand reads (8 rows x
-// 16 bytes per lane octet) hit all 32 banks once.
+// Tiling (TileCfg): large problems use a 256 x 256 output tile per
+// 256-thread workgroup, 2 x 2 waves of 128 x 128 (a 4 x 4 grid of 32x32x16
+// MFMAs each, 256 FP32 accumulators per lane), K step 64 and a double-
+// buffered LDS stage of 2 x 64 KB; small problems a 128 x 128 tile of 4
+// waves of 64 x 64.  Operand fragments are read from LDS one k16 step ahead
+// of the MFMAs that use them; the next K step's global loads are issued
+// before the current step's MFMAs.  LDS rows are 64 halves = eight 16-byte
+// chunks; chunk c of row r lives at slot c ^ (r & 7), so the MFMA operand
+// reads (8 rows x 16 bytes per lane octet) touch every bank once.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -26,15 +30,23 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int NT = 256;
-constexpr int TILE = BM * BK;  // 16-bit elements per operand tile (BM == BN)
-static_assert(BM == BN, "loaders assume square tiles");
+constexpr int BK = 64;  // K elements per pipeline step (four NVFP4 blocks)
+
+template <int BM_, int BN_, int WGM_, int WGN_, int MINB_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, MINB = MINB_;
+    static constexpr int NT = WGM * WGN * 64;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
+    static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA tiles per wave
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+};
+using BigTile = TileCfg<256, 256, 2, 2, 1>;
+using SmallTile = TileCfg<128, 128, 2, 2, 2>;
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
 struct GemmArgs {
-    const void *a;          // A codes, A BF16
+    const void *a;          // A codes or A BF16
     const uint8_t *a_scales;
     const float *a_alpha;
     const void *w;          // W codes or W BF16
@@ -46,90 +58,138 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------- loaders
-// Every loader moves one [128 rows x 64 k] operand tile: thread t owns row
-// t >> 1 and k-half (t & 1) * 32 .. +32, i.e. two NVFP4 blocks.
+// A loader moves one [R rows x 64 k] operand tile with NT threads; each thread
+// owns EPT = R * 64 / NT consecutive k of one row (32 or 64: two or four
+// NVFP4 blocks).
 
-struct Fp4Stage {
-    uint4 codes;
-    uint32_t sc;  // two scale bytes
+template <int R, int NT>
+struct Part {
+    static constexpr int EPT = R * BK / NT;
+    static constexpr int PER_ROW = BK / EPT;
+    static_assert(EPT == 32 || EPT == 64, "unsupported loader split");
+    __device__ __forceinline__ static int row() { return threadIdx.x / PER_ROW; }
+    __device__ __forceinline__ static int part() { return threadIdx.x % PER_ROW; }
 };
 
-__device__ __forceinline__ void fp4_load(Fp4Stage &st, const uint8_t *__restrict__ codes,
-                                         const uint8_t *__restrict__ scales, int64_t rows, int64_t K,
-                                         int64_t row0, int kt) {
-    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
-    const int64_t row = row0 + r;
-    const int64_t k0 = (int64_t)kt * BK + h * 32;
-    st.codes = make_uint4(0, 0, 0, 0);
-    st.sc = 0;
-    if (row < rows) {
+template <int EPT>
+struct Fp4Stage {
+    uint4 codes[EPT / 32];
+    uint32_t sc;  // EPT/16 scale bytes
+};
+
+template <int R, int NT, bool kGuard>
+__device__ __forceinline__ void fp4_load(Fp4Stage<Part<R, NT>::EPT> &st, const uint8_t *__restrict__ codes,
+                                         const uint8_t *__restrict__ scales, int64_t rows, int64_t K, int64_t row0,
+                                         int kt) {
+    constexpr int EPT = Part<R, NT>::EPT;
+    const int64_t row = row0 + Part<R, NT>::row();
+    const int64_t k0 = (int64_t)kt * BK + Part<R, NT>::part() * EPT;
+    if (!kGuard) {  // interior tile, K % 64 == 0: every access is in range
         const uint8_t *cp = codes + row * (K >> 1) + (k0 >> 1);
+#pragma unroll
+        for (int i = 0; i < EPT / 32; ++i) st.codes[i] = *reinterpret_cast<const uint4 *>(cp + 16 * i);
         const uint8_t *sp = scales + row * (K >> 4) + (k0 >> 4);
-        if (k0 + 32 <= K) {
-            if ((K & 31) == 0) {
-                st.codes = *reinterpret_cast<const uint4 *>(cp);
+        st.sc = EPT == 64 ? *reinterpret_cast<const uint32_t *>(sp) : *reinterpret_cast<const uint16_t *>(sp);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < EPT / 32; ++i) st.codes[i] = make_uint4(0, 0, 0, 0);
+    st.sc = 0;
+    if (row >= rows) return;
+    const uint8_t *cp = codes + row * (K >> 1) + (k0 >> 1);
+    const uint8_t *sp = scales + row * (K >> 4) + (k0 >> 4);
+    if (k0 + EPT <= K && (K & 63) == 0) {
+        // whole chunk in range; 16-byte code loads and one aligned scale word
+#pragma unroll
+        for (int i = 0; i < EPT / 32; ++i) st.codes[i] = *reinterpret_cast<const uint4 *>(cp + 16 * i);
+        if (EPT == 64)
+            st.sc = *reinterpret_cast<const uint32_t *>(sp);
+        else
+            st.sc = *reinterpret_cast<const uint16_t *>(sp);
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < EPT / 16; ++b) {  // block by block, 8 code bytes each
+        if (k0 + 16 * b + 16 <= K) {
+            const uint2 c = *reinterpret_cast<const uint2 *>(cp + 8 * b);
+            if (b & 1) {
+                st.codes[b >> 1].z = c.x;
+                st.codes[b >> 1].w = c.y;
             } else {
-                uint2 lo = *reinterpret_cast<const uint2 *>(cp), hi = *reinterpret_cast<const uint2 *>(cp + 8);
-                st.codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                st.codes[b >> 1].x = c.x;
+                st.codes[b >> 1].y = c.y;
             }
-            st.sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
-        } else if (k0 + 16 <= K) {
-            uint2 lo = *reinterpret_cast<const uint2 *>(cp);
-            st.codes = make_uint4(lo.x, lo.y, 0, 0);
-            st.sc = sp[0];
+            st.sc |= (uint32_t)sp[b] << (8 * b);
         }
     }
 }
 
-// 8 E2M1 codes (one 32-bit word) times sigma -> 8 FP16 values (exact).
-__device__ __forceinline__ half8_t expand8(uint32_t w, half_t sigma) {
-    half8_t v;
+// 8 E2M1 codes (one 32-bit word, element 0 in the low nibble) times sigma ->
+// 8 FP16 values, exactly: the hardware converts FP4 pairs to FP16 (scale 1),
+// then a packed FP16 multiply applies sigma (q * sigma has <= 6 significant
+// bits and lies in [2^-10, 2688], so the product is exact).
+__device__ __forceinline__ half8_t expand8(uint32_t w, half2_t sig2) {
+    half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sig2;
+    half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sig2;
+    half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sig2;
+    half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sig2;
+    return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int R, int NT>
+__device__ __forceinline__ void fp4_store(const Fp4Stage<Part<R, NT>::EPT> &st, half_t *lds) {
+    constexpr int EPT = Part<R, NT>::EPT;
+    const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint16_t b = (uint16_t)e2m1_to_f16_bits((w >> (4 * i)) & 15u);
-        v[i] = __builtin_bit_cast(half_t, b) * sigma;
+    for (int b = 0; b < EPT / 16; ++b) {
+        const half_t s = e4m3_to_f16((st.sc >> (8 * b)) & 0xFFu);
+        const half2_t s2 = half2_t{s, s};
+        const uint4 &q = st.codes[b >> 1];
+        const uint32_t w0 = (b & 1) ? q.z : q.x, w1 = (b & 1) ? q.w : q.y;
+        *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b)) = expand8(w0, s2);
+        *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b + 1)) = expand8(w1, s2);
     }
-    return v;
 }
 
-__device__ __forceinline__ void fp4_store(const Fp4Stage &st, half_t *lds) {
-    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
-    const half_t s0 = e4m3_to_f16(st.sc & 0xFFu), s1 = e4m3_to_f16(st.sc >> 8);
-    const uint32_t w[4] = {st.codes.x, st.codes.y, st.codes.z, st.codes.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<half8_t *>(lds + lds_off(r, h * 4 + c)) = expand8(w[c], c < 2 ? s0 : s1);
-}
-
+template <int EPT>
 struct Bf16Stage {
-    uint4 v[4];  // 32 BF16 values
+    u32x4_t v[EPT / 8];
 };
 
-__device__ __forceinline__ void bf16_load(Bf16Stage &st, const uint16_t *__restrict__ x, int64_t ld, int64_t rows,
-                                          int64_t K, int64_t row0, int kt) {
-    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
-    const int64_t row = row0 + r;
-    const int64_t k0 = (int64_t)kt * BK + h * 32;
+template <int R, int NT, bool kGuard>
+__device__ __forceinline__ void bf16_load(Bf16Stage<Part<R, NT>::EPT> &st, const uint16_t *__restrict__ x, int64_t ld,
+                                          int64_t rows, int64_t K, int64_t row0, int kt) {
+    constexpr int EPT = Part<R, NT>::EPT;
+    const int64_t row = row0 + Part<R, NT>::row();
+    const int64_t k0 = (int64_t)kt * BK + Part<R, NT>::part() * EPT;
+    if (!kGuard) {  // interior tile, K % 64 == 0
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        st.v[c] = make_uint4(0, 0, 0, 0);
-        if (row < rows && k0 + 8 * c + 8 <= K)
-            st.v[c] = *reinterpret_cast<const uint4 *>(x + row * ld + k0 + 8 * c);
+        for (int c = 0; c < EPT / 8; ++c) st.v[c] = *reinterpret_cast<const u32x4_t *>(x + row * ld + k0 + 8 * c);
+        return;
     }
+    const bool rin = row < rows;
+    const uint16_t *p = x + (rin ? row : 0) * ld + k0;
+#pragma unroll
+    for (int c = 0; c < EPT / 8; ++c)
+        st.v[c] = (rin && k0 + 8 * c + 8 <= K) ? *reinterpret_cast<const u32x4_t *>(p + 8 * c) : u32x4_t{0, 0, 0, 0};
 }
 
-__device__ __forceinline__ void bf16_store(const Bf16Stage &st, uint16_t *lds) {
-    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+template <int R, int NT>
+__device__ __forceinline__ void bf16_store(const Bf16Stage<Part<R, NT>::EPT> &st, uint16_t *lds) {
+    constexpr int EPT = Part<R, NT>::EPT;
+    const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4 *>(lds + lds_off(r, h * 4 + c)) = st.v[c];
+    for (int c = 0; c < EPT / 8; ++c) *reinterpret_cast<u32x4_t *>(lds + lds_off(r, c0 + c)) = st.v[c];
 }
 
 // Fused prologue: quantize the staged BF16 values exactly as the standalone
 // quantizer does (same block_scale / quant_elem), then expand q * sigma.
-__device__ __forceinline__ void fused_store(const Bf16Stage &st, half_t *lds, float alpha) {
-    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+template <int R, int NT>
+__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, float alpha) {
+    constexpr int EPT = Part<R, NT>::EPT;
+    const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < EPT / 16; ++b) {
         const uint32_t w[8] = {st.v[2 * b].x, st.v[2 * b].y, st.v[2 * b].z, st.v[2 * b].w,
                                st.v[2 * b + 1].x, st.v[2 * b + 1].y, st.v[2 * b + 1].z, st.v[2 * b + 1].w};
         uint32_t am = 0;
@@ -137,6 +197,7 @@ __device__ __forceinline__ void fused_store(const Bf16Stage &st, half_t *lds, fl
         for (int i = 0; i < 8; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
         const BlockScale bs = block_scale(bf16_bits_to_f32(am), alpha);
         const half_t sig = (half_t)bs.sigma;
+        const half2_t s2 = half2_t{sig, sig};
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             uint32_t packed = 0;
@@ -146,7 +207,7 @@ __device__ __forceinline__ void fused_store(const Bf16Stage &st, half_t *lds, fl
                 packed |= quant_elem(bf16_bits_to_f32(x & 0xFFFFu), bs.d) << (8 * i);
                 packed |= quant_elem(bf16_bits_to_f32(x >> 16), bs.d) << (8 * i + 4);
             }
-            *reinterpret_cast<half8_t *>(lds + lds_off(r, h * 4 + 2 * b + c)) = expand8(packed, sig);
+            *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b + c)) = expand8(packed, s2);
         }
     }
 }
@@ -154,8 +215,9 @@ __device__ __forceinline__ void fused_store(const Bf16Stage &st, half_t *lds, fl
 // ---------------------------------------------------------------- kernel
 enum Kind { KIND_NVFP4 = 0, KIND_FUSED = 1, KIND_BF16 = 2 };
 
+template <class C>
 __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int &tm, int &tn) {
-    const int num_tm = (int)((M + BM - 1) / BM), num_tn = (int)((N + BN - 1) / BN);
+    const int num_tm = (int)((M + C::BM - 1) / C::BM), num_tn = (int)((N + C::BN - 1) / C::BN);
     const int nb = gridDim.x;
     int bid = blockIdx.x;
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
@@ -171,91 +233,162 @@ __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int &tm, int &
     tn = in / gsize;
 }
 
-template <int kKind, bool kOutBf16>
-__global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmArgs g) {
-    typedef typename std::conditional<kKind == KIND_BF16, uint16_t, half_t>::type lds_t;
-    __shared__ __attribute__((aligned(16))) lds_t lds[2][2][TILE];
+// Register stage of one pipeline step, per operand kind: A then W.
+template <class SA, class SW>
+struct StagePair {
+    SA a;
+    SW w;
+};
+template <int kKind, int EA, int EW>
+struct StageSel {
+    typedef StagePair<Fp4Stage<EA>, Fp4Stage<EW>> type;
+};
+template <int EA, int EW>
+struct StageSel<KIND_FUSED, EA, EW> {
+    typedef StagePair<Bf16Stage<EA>, Fp4Stage<EW>> type;
+};
+template <int EA, int EW>
+struct StageSel<KIND_BF16, EA, EW> {
+    typedef StagePair<Bf16Stage<EA>, Bf16Stage<EW>> type;
+};
 
-    int tm, tn;
-    tile_coords(g.M, g.N, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+template <int kKind>
+struct KindTraits {
+    typedef half_t lds_t;
+};
+template <>
+struct KindTraits<KIND_BF16> {
+    typedef uint16_t lds_t;
+};
+
+// One output tile.  kGuard = false is the interior fast path (whole tile in
+// range and K % 64 == 0): no bounds checks, so each pipeline step is one
+// basic block the scheduler can interleave.  NVFP4 operands are prefetched
+// two K steps ahead in registers (18 VGPRs a stage); BF16 operands one step.
+template <class C, int kKind, bool kOutBf16, bool kGuard>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t n0,
+                                          typename KindTraits<kKind>::lds_t *lds) {
+    typedef typename KindTraits<kKind>::lds_t lds_t;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT, TM = C::TM, TN = C::TN;
+    constexpr int KS = BK / 16;  // k16 MFMA steps per pipeline step
+    auto As = [&](int s) __attribute__((always_inline)) { return lds + s * (BM + BN) * BK; };
+    auto Ws = [&](int s) __attribute__((always_inline)) { return lds + s * (BM + BN) * BK + BM * BK; };
+
     const int KT = (int)((g.K + BK - 1) / BK);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
+    // row limits seen by the loaders: the real ones, or "infinite" on the fast path
 
     float a_alpha = 1.0f;
     if (kKind == KIND_FUSED) a_alpha = *g.a_alpha;
 
-    Fp4Stage sa4, sw4;
-    Bf16Stage sab, swb;
+    typedef typename StageSel<kKind, Part<BM, NT>::EPT, Part<BN, NT>::EPT>::type Stage;
 
-    auto load = [&](int kt) {
-        if (kKind == KIND_NVFP4)
-            fp4_load(sa4, (const uint8_t *)g.a, g.a_scales, g.M, g.K, m0, kt);
-        else
-            bf16_load(sab, (const uint16_t *)g.a, g.lda, g.M, g.K, m0, kt);
-        if (kKind == KIND_BF16)
-            bf16_load(swb, (const uint16_t *)g.w, g.K, g.N, g.K, n0, kt);
-        else
-            fp4_load(sw4, (const uint8_t *)g.w, g.w_scales, g.N, g.K, n0, kt);
+    // load half p (0: A, 1: W) of pipeline step kt into the register stage
+    auto load_part = [&](Stage &st, int kt, int p) __attribute__((always_inline)) {
+        if (p == 0) {
+            if constexpr (kKind == KIND_NVFP4)
+                fp4_load<BM, NT, kGuard>(st.a, (const uint8_t *)g.a, g.a_scales, g.M, g.K, m0, kt);
+            else
+                bf16_load<BM, NT, kGuard>(st.a, (const uint16_t *)g.a, g.lda, g.M, g.K, m0, kt);
+        } else {
+            if constexpr (kKind == KIND_BF16)
+                bf16_load<BN, NT, kGuard>(st.w, (const uint16_t *)g.w, g.K, g.N, g.K, n0, kt);
+            else
+                fp4_load<BN, NT, kGuard>(st.w, (const uint8_t *)g.w, g.w_scales, g.N, g.K, n0, kt);
+        }
     };
-    auto store = [&](int buf) {
-        if (kKind == KIND_NVFP4) fp4_store(sa4, (half_t *)lds[buf][0]);
-        if (kKind == KIND_FUSED) fused_store(sab, (half_t *)lds[buf][0], a_alpha);
-        if (kKind == KIND_BF16) bf16_store(sab, (uint16_t *)lds[buf][0]);
-        if (kKind == KIND_BF16)
-            bf16_store(swb, (uint16_t *)lds[buf][1]);
-        else
-            fp4_store(sw4, (half_t *)lds[buf][1]);
+    // store part p (of 2) of a stage into LDS buffer s
+    auto store_part = [&](const Stage &st, int s, int p) __attribute__((always_inline)) {
+        if (p == 0) {
+            if constexpr (kKind == KIND_NVFP4) fp4_store<BM, NT>(st.a, (half_t *)As(s));
+            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT>(st.a, (half_t *)As(s), a_alpha);
+            if constexpr (kKind == KIND_BF16) bf16_store<BM, NT>(st.a, (uint16_t *)As(s));
+        } else {
+            if constexpr (kKind == KIND_BF16)
+                bf16_store<BN, NT>(st.w, (uint16_t *)Ws(s));
+            else
+                fp4_store<BN, NT>(st.w, (half_t *)Ws(s));
+        }
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    uint4 af[2][TM], bf[2][TN];
+    auto read_frags = [&](int s, int ks, uint4 *fa, uint4 *fb) __attribute__((always_inline)) {
+        const lds_t *A = As(s);
+        const lds_t *W = Ws(s);
+        const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[i] = *reinterpret_cast<const uint4 *>(A + lds_off(wm * C::WM + i * 32 + (lane & 31), chunk));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[j] = *reinterpret_cast<const uint4 *>(W + lds_off(wn * C::WN + j * 32 + (lane & 31), chunk));
+    };
+    auto mfmas = [&](const uint4 *fa, const uint4 *fb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if (kKind == KIND_BF16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
+                                                                        __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j],
+                                                                        0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, fa[i]),
+                                                                       __builtin_bit_cast(half8_t, fb[j]), acc[i][j],
+                                                                       0, 0, 0);
+            }
+    };
+    // Pipeline step kt computes on LDS buffer kt & 1.  The register stage then
+    // holds step kt + 1 (loaded one step earlier): its A half is staged into
+    // buffer (kt + 1) & 1 during the first k16 MFMA group and its W half
+    // during the second, and each half is reloaded with step kt + 2 right
+    // after it has been consumed, so global loads get a full step to land.
+    Stage st;
+    auto step = [&](int kt, bool do_store, bool do_load) __attribute__((always_inline)) {
+        const int cur = kt & 1;
+        read_frags(cur, 0, af[0], bf[0]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            if (ks == 0 && do_store) store_part(st, cur ^ 1, 0);
+            if (ks == 1 && do_load) load_part(st, kt + 2, 0);
+            if (ks == 1 && do_store) store_part(st, cur ^ 1, 1);
+            if (ks == 2 && do_load) load_part(st, kt + 2, 1);
+            mfmas(af[ks & 1], bf[ks & 1]);
+        }
+    };
+
     if (KT > 0) {
-        load(0);
-        store(0);
+        load_part(st, 0, 0);
+        load_part(st, 0, 1);
+        store_part(st, 0, 0);
+        store_part(st, 0, 1);
+        if (KT > 1) {
+            load_part(st, 1, 0);
+            load_part(st, 1, 1);
+        }
     }
     __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load(kt + 1);
-        const lds_t *As = lds[cur][0];
-        const lds_t *Ws = lds[cur][1];
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int chunk = 2 * ks + (lane >> 5);
-            uint4 af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ra = wm * 64 + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const uint4 *>(As + lds_off(ra, chunk));
-                const int rb = wn * 64 + i * 32 + (lane & 31);
-                bf[i] = *reinterpret_cast<const uint4 *>(Ws + lds_off(rb, chunk));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (kKind == KIND_BF16)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
-                                                                            __builtin_bit_cast(bf16x8_t, bf[j]),
-                                                                            acc[i][j], 0, 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, af[i]),
-                                                                           __builtin_bit_cast(half8_t, bf[j]),
-                                                                           acc[i][j], 0, 0, 0);
-                }
-        }
-        if (kt + 1 < KT) store(cur ^ 1);
+    int kt = 0;
+    for (; kt + 2 < KT; ++kt) {
+        step(kt, true, true);
         __syncthreads();
     }
+    if (kt + 1 < KT) {
+        step(kt, true, false);
+        __syncthreads();
+        ++kt;
+    }
+    if (kt < KT) step(kt, false, false);
 
     // epilogue: y = (acc * alphaA) * alphaW, stored FP32 or BF16 (nearest-even)
     float sa = 1.0f, sw = 1.0f;
@@ -264,36 +397,64 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmArgs g) {
         sw = *g.w_alpha;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-            if (col >= g.N) continue;
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn * C::WN + j * 32 + (lane & 31);
+            if (kGuard && col >= g.N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row >= g.M) continue;
+                const int64_t row = m0 + wm * C::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (kGuard && row >= g.M) continue;
                 float y = acc[i][j][r];
                 if (kKind != KIND_BF16) y = (y * sa) * sw;
                 if (kOutBf16)
-                    reinterpret_cast<uint16_t *>(g.out)[row * g.ld_out + col] = (uint16_t)f32_to_bf16_bits(y);
+                    reinterpret_cast<__bf16 *>(g.out)[row * g.ld_out + col] = (__bf16)y;
                 else
                     reinterpret_cast<float *>(g.out)[row * g.ld_out + col] = y;
             }
         }
 }
 
-template <int kKind>
-hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
-    const int64_t num_tm = (g.M + BM - 1) / BM, num_tn = (g.N + BN - 1) / BN;
-    const int64_t nb = num_tm * num_tn;
+template <class C, int kKind, bool kOutBf16>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_kernel(GemmArgs g) {
+    typedef typename KindTraits<kKind>::lds_t lds_t;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    lds_t *lds = reinterpret_cast<lds_t *>(smem);
+    int tm, tn;
+    tile_coords<C>(g.M, g.N, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const bool full = m0 + C::BM <= g.M && n0 + C::BN <= g.N && (g.K & (BK - 1)) == 0;
+    if (full)
+        gemm_tile<C, kKind, kOutBf16, false>(g, m0, n0, lds);
+    else
+        gemm_tile<C, kKind, kOutBf16, true>(g, m0, n0, lds);
+}
+
+template <class C, int kKind, bool kOutBf16>
+hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
+    const int64_t nb = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
     if (nb <= 0) return hipSuccess;
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (out_type == OUT_BF16)
-        hipLaunchKernelGGL((gemm_kernel<kKind, true>), dim3((unsigned)nb), dim3(NT), 0, s, g);
-    else
-        hipLaunchKernelGGL((gemm_kernel<kKind, false>), dim3((unsigned)nb), dim3(NT), 0, s, g);
+    const size_t lds_bytes = (size_t)2 * (C::BM + C::BN) * BK * 2;
+    auto kern = gemm_kernel<C, kKind, kOutBf16>;
+    static bool attr_set = false;  // benign race: setting it twice is harmless
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds_bytes, s, g);
     return hipGetLastError();
+}
+
+template <int kKind>
+hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
+    // the 256 x 256 tile once there are enough tiles to fill the 256 CUs
+    const bool big = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256;
+    if (big)
+        return out_type == OUT_BF16 ? launch_cfg<BigTile, kKind, true>(g, s) : launch_cfg<BigTile, kKind, false>(g, s);
+    return out_type == OUT_BF16 ? launch_cfg<SmallTile, kKind, true>(g, s) : launch_cfg<SmallTile, kKind, false>(g, s);
 }
 
 }  // namespace
