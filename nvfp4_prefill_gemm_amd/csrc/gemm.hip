@@ -15,14 +15,18 @@
 // staging step.
 //
 // Tiling (TileCfg): large problems use a 256 x 256 output tile per
-// 256-thread workgroup, 2 x 2 waves of 128 x 128 (a 4 x 4 grid of 32x32x16
-// MFMAs each, 256 FP32 accumulators per lane), K step 64 and a double-
+// 512-thread workgroup, 2 x 4 waves of 128 x 64 (a 4 x 2 grid of 32x32x16
+// MFMAs each, 128 FP32 accumulators per lane; two waves per SIMD, so one
+// wave's staging work overlaps the other's MFMAs), K step 64 and a double-
 // buffered LDS stage of 2 x 64 KB; small problems a 128 x 128 tile of 4
 // waves of 64 x 64.  Operand fragments are read from LDS one k16 step ahead
 // of the MFMAs that use them; the next K step's global loads are issued
 // before the current step's MFMAs.  LDS rows are 64 halves = eight 16-byte
 // chunks; chunk c of row r lives at slot c ^ (r & 7), so the MFMA operand
 // reads (8 rows x 16 bytes per lane octet) touch every bank once.
+#include <stdlib.h>
+#include <string.h>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -40,8 +44,9 @@ struct TileCfg {
     static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA tiles per wave
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 };
-using BigTile = TileCfg<256, 256, 2, 2, 1>;
-using SmallTile = TileCfg<128, 128, 2, 2, 2>;
+using BigTile = TileCfg<256, 256, 2, 2, 1>;   // 4 waves of 128 x 128
+using BigTile8 = TileCfg<256, 256, 2, 4, 1>;  // 8 waves of 128 x 64
+using SmallTile = TileCfg<128, 128, 2, 2, 2>; // 4 waves of 64 x 64
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
@@ -125,15 +130,25 @@ __device__ __forceinline__ void fp4_load(Fp4Stage<Part<R, NT>::EPT> &st, const u
 }
 
 // 8 E2M1 codes (one 32-bit word, element 0 in the low nibble) times sigma ->
-// 8 FP16 values, exactly: the hardware converts FP4 pairs to FP16 (scale 1),
-// then a packed FP16 multiply applies sigma (q * sigma has <= 6 significant
-// bits and lies in [2^-10, 2688], so the product is exact).
+// 8 FP16 values, exactly.  The hardware converts FP4 pairs to FP16 with a
+// power-of-two scale of 2^8; sig2 holds sigma * 2^-8 in both halves, and one
+// packed FP16 multiply forms q * sigma.  Every factor is exact in FP16 and so
+// is the product (q * sigma has <= 6 significant bits, in [2^-10, 2688]).
 __device__ __forceinline__ half8_t expand8(uint32_t w, half2_t sig2) {
-    half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sig2;
-    half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sig2;
-    half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sig2;
-    half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sig2;
+    half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * sig2;
+    half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * sig2;
+    half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * sig2;
+    half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * sig2;
     return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// sigma * 2^-8 as FP16, in both halves, from an E4M3 code (sign clear).
+// Read as FP16 bits, code << 7 lines E4M3's exponent field up with FP16's
+// (bias 15 = 7 + 8) and its three mantissa bits with FP16's top three, and
+// E4M3 subnormals m * 2^-9 land on FP16 subnormals m * 2^-17; so the value is
+// exactly sigma * 2^-8 for every finite code, with no branch.
+__device__ __forceinline__ half2_t e4m3_to_f16x2_over256(uint32_t c) {
+    return __builtin_bit_cast(half2_t, (c << 7) | (c << 23));
 }
 
 template <int R, int NT>
@@ -142,8 +157,7 @@ __device__ __forceinline__ void fp4_store(const Fp4Stage<Part<R, NT>::EPT> &st, 
     const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
     for (int b = 0; b < EPT / 16; ++b) {
-        const half_t s = e4m3_to_f16((st.sc >> (8 * b)) & 0xFFu);
-        const half2_t s2 = half2_t{s, s};
+        const half2_t s2 = e4m3_to_f16x2_over256((st.sc >> (8 * b)) & 0xFFu);
         const uint4 &q = st.codes[b >> 1];
         const uint32_t w0 = (b & 1) ? q.z : q.x, w1 = (b & 1) ? q.w : q.y;
         *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b)) = expand8(w0, s2);
@@ -196,8 +210,7 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
         const BlockScale bs = block_scale(bf16_bits_to_f32(am), alpha);
-        const half_t sig = (half_t)bs.sigma;
-        const half2_t s2 = half2_t{sig, sig};
+        const half2_t s2 = e4m3_to_f16x2_over256(bs.code);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             uint32_t packed = 0;
@@ -448,13 +461,29 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Tile choice: NVFP4_GEMM_TILE=big4|big8|small overrides (tuning knob);
+// default: a 256 x 256 tile once there are enough tiles to fill the 256 CUs.
+int tile_override() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("NVFP4_GEMM_TILE");
+        v = !e ? 0 : !strcmp(e, "big4") ? 1 : !strcmp(e, "big8") ? 2 : !strcmp(e, "small") ? 3 : 0;
+    }
+    return v;
+}
+
+template <class C, int kKind>
+hipError_t launch_out(const GemmArgs &g, int out_type, hipStream_t s) {
+    return out_type == OUT_BF16 ? launch_cfg<C, kKind, true>(g, s) : launch_cfg<C, kKind, false>(g, s);
+}
+
 template <int kKind>
 hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
-    // the 256 x 256 tile once there are enough tiles to fill the 256 CUs
-    const bool big = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256;
-    if (big)
-        return out_type == OUT_BF16 ? launch_cfg<BigTile, kKind, true>(g, s) : launch_cfg<BigTile, kKind, false>(g, s);
-    return out_type == OUT_BF16 ? launch_cfg<SmallTile, kKind, true>(g, s) : launch_cfg<SmallTile, kKind, false>(g, s);
+    int t = tile_override();
+    if (t == 0) t = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256 ? 2 : 3;
+    if (t == 1) return launch_out<BigTile, kKind>(g, out_type, s);
+    if (t == 2) return launch_out<BigTile8, kKind>(g, out_type, s);
+    return launch_out<SmallTile, kKind>(g, out_type, s);
 }
 
 }  // namespace

@@ -81,6 +81,26 @@ def test_ragged_shapes(nv, oracle_mod, M, N, K):
     _check_both_outputs(_gemm(nv, A, W, "f32"), _gemm(nv, A, W, "bf16"), ref, f"{M}x{N}x{K}")
 
 
+def test_extreme_scale_codes(nv, oracle_mod):
+    """Random E2M1 codes with every E4M3 scale code that can occur: the seven
+    subnormals (m * 2^-9), 448, and zero blocks; tiny and large tensor scales."""
+    g = np.random.default_rng(31)
+    M, N, K = 160, 288, 512
+    qa = g.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    qw = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sa = g.integers(0, 127, size=(M, K // 16)).astype(np.uint8)
+    sw = g.integers(0, 127, size=(N, K // 16)).astype(np.uint8)
+    sa[:, :8] = np.arange(8, dtype=np.uint8)[None, :]  # 0 and the subnormals
+    sw[:, 8:16] = np.arange(8, dtype=np.uint8)[None, :]
+    sa[::3, 20] = 0x7E
+    sw[::5, 20] = 0x7E
+    for aa, aw in ((1.0, 1.0), (np.float32(3.1e-3), np.float32(7.6e-6)), (np.float32(2.0 ** -20), np.float32(1024.0))):
+        A, W = (qa, sa, np.float32(aa)), (qw, sw, np.float32(aw))
+        ref = oracle_mod.gemm_exact(*A, *W)
+        say("nvfp4 gemm extreme scale codes", aa, aw)
+        _check_both_outputs(_gemm(nv, A, W, "f32"), _gemm(nv, A, W, "bf16"), ref, f"extreme scales {aa},{aw}")
+
+
 def test_k_zero_and_empty(nv):
     import torch
 
