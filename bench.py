@@ -41,6 +41,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--no-extras", action="store_true", help="only the headline NVFP4 prefill timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle leg")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
 
 
@@ -158,6 +160,12 @@ def main():
             if timer:
                 eg.record()
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         nvfp4_step()
     torch.cuda.synchronize()

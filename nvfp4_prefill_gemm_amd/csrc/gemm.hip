@@ -22,10 +22,12 @@
 // waves of 64 x 64.  Operand fragments are read from LDS one k16 step ahead
 // of the MFMAs that use them; the next K step's global loads are issued
 // before the current step's MFMAs.  LDS rows are 64 halves = eight 16-byte
-// chunks; chunk c of row r lives at slot c ^ (r & 7), so the MFMA operand
-// reads (8 rows x 16 bytes per lane octet) touch every bank once.
+// chunks, swizzled (lds_off) so operand reads and staging writes are free of
+// bank conflicts.
 #include <stdlib.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
@@ -48,7 +50,20 @@ using BigTile = TileCfg<256, 256, 2, 2, 1>;   // 4 waves of 128 x 128
 using BigTile8 = TileCfg<256, 256, 2, 4, 1>;  // 8 waves of 128 x 64
 using SmallTile = TileCfg<128, 128, 2, 2, 2>; // 4 waves of 64 x 64
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// LDS tile layout: row-major rows of 64 halves (eight 16-byte chunks); chunk c
+// of row r sits in slot c ^ f(r).  Measured on gfx950, 16-byte LDS reads are
+// served 16 lanes per cycle across 64 banks (two 128-byte rows) and 16-byte
+// writes 8 lanes per cycle across 32 banks (one row).  An MFMA operand read
+// touches 16 consecutive rows (16-aligned) at one chunk, so f must be one-to-
+// one on the even rows and on the odd rows of each 16-row group; a staging
+// write touches 4 consecutive rows (4-aligned) at chunks {k, k + 4}, so f's
+// low two bits must differ across each 4-row group.  f(r) = s((r >> 1) & 7)
+// ^ (r & 1), with s swapping bits 0 and 1, satisfies both.
+__device__ __forceinline__ int lds_swz(int row) {
+    const int m = (row >> 1) & 7;
+    return (((m & 1) << 1) | ((m >> 1) & 1) | (m & 4)) ^ (row & 1);
+}
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ lds_swz(row)) << 3); }
 
 struct GemmArgs {
     const void *a;          // A codes or A BF16
@@ -151,12 +166,14 @@ __device__ __forceinline__ half2_t e4m3_to_f16x2_over256(uint32_t c) {
     return __builtin_bit_cast(half2_t, (c << 7) | (c << 23));
 }
 
-template <int R, int NT>
+// H selects which half of the thread's blocks to stage (-1: all of them)
+template <int R, int NT, int H = -1>
 __device__ __forceinline__ void fp4_store(const Fp4Stage<Part<R, NT>::EPT> &st, half_t *lds) {
     constexpr int EPT = Part<R, NT>::EPT;
+    constexpr int NB = EPT / 16, B0 = H < 0 ? 0 : H * NB / 2, B1 = H < 0 ? NB : (H + 1) * NB / 2;
     const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int b = 0; b < EPT / 16; ++b) {
+    for (int b = B0; b < B1; ++b) {
         const half2_t s2 = e4m3_to_f16x2_over256((st.sc >> (8 * b)) & 0xFFu);
         const uint4 &q = st.codes[b >> 1];
         const uint32_t w0 = (b & 1) ? q.z : q.x, w1 = (b & 1) ? q.w : q.y;
@@ -188,22 +205,24 @@ __device__ __forceinline__ void bf16_load(Bf16Stage<Part<R, NT>::EPT> &st, const
         st.v[c] = (rin && k0 + 8 * c + 8 <= K) ? *reinterpret_cast<const u32x4_t *>(p + 8 * c) : u32x4_t{0, 0, 0, 0};
 }
 
-template <int R, int NT>
+template <int R, int NT, int H = -1>
 __device__ __forceinline__ void bf16_store(const Bf16Stage<Part<R, NT>::EPT> &st, uint16_t *lds) {
     constexpr int EPT = Part<R, NT>::EPT;
+    constexpr int NC = EPT / 8, C0 = H < 0 ? 0 : H * NC / 2, C1 = H < 0 ? NC : (H + 1) * NC / 2;
     const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int c = 0; c < EPT / 8; ++c) *reinterpret_cast<u32x4_t *>(lds + lds_off(r, c0 + c)) = st.v[c];
+    for (int c = C0; c < C1; ++c) *reinterpret_cast<u32x4_t *>(lds + lds_off(r, c0 + c)) = st.v[c];
 }
 
 // Fused prologue: quantize the staged BF16 values exactly as the standalone
 // quantizer does (same block_scale / quant_elem), then expand q * sigma.
-template <int R, int NT>
+template <int R, int NT, int H = -1>
 __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, float alpha) {
     constexpr int EPT = Part<R, NT>::EPT;
+    constexpr int NB = EPT / 16, B0 = H < 0 ? 0 : H * NB / 2, B1 = H < 0 ? NB : (H + 1) * NB / 2;
     const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int b = 0; b < EPT / 16; ++b) {
+    for (int b = B0; b < B1; ++b) {
         const uint32_t w[8] = {st.v[2 * b].x, st.v[2 * b].y, st.v[2 * b].z, st.v[2 * b].w,
                                st.v[2 * b + 1].x, st.v[2 * b + 1].y, st.v[2 * b + 1].z, st.v[2 * b + 1].w};
         uint32_t am = 0;
@@ -311,18 +330,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
                 fp4_load<BN, NT, kGuard>(st.w, (const uint8_t *)g.w, g.w_scales, g.N, g.K, n0, kt);
         }
     };
-    // store part p (of 2) of a stage into LDS buffer s
-    auto store_part = [&](const Stage &st, int s, int p) __attribute__((always_inline)) {
-        if (p == 0) {
-            if constexpr (kKind == KIND_NVFP4) fp4_store<BM, NT>(st.a, (half_t *)As(s));
-            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT>(st.a, (half_t *)As(s), a_alpha);
-            if constexpr (kKind == KIND_BF16) bf16_store<BM, NT>(st.a, (uint16_t *)As(s));
+    // stage quarter q of a register stage into LDS buffer s: A's first and
+    // second half of blocks (q = 0, 1), then W's (q = 2, 3)
+    auto store_q = [&](const Stage &st, int s, auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int h = q & 1;
+        if constexpr (q < 2) {
+            if constexpr (kKind == KIND_NVFP4) fp4_store<BM, NT, h>(st.a, (half_t *)As(s));
+            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT, h>(st.a, (half_t *)As(s), a_alpha);
+            if constexpr (kKind == KIND_BF16) bf16_store<BM, NT, h>(st.a, (uint16_t *)As(s));
         } else {
             if constexpr (kKind == KIND_BF16)
-                bf16_store<BN, NT>(st.w, (uint16_t *)Ws(s));
+                bf16_store<BN, NT, h>(st.w, (uint16_t *)Ws(s));
             else
-                fp4_store<BN, NT>(st.w, (half_t *)Ws(s));
+                fp4_store<BN, NT, h>(st.w, (half_t *)Ws(s));
         }
+    };
+    auto store_all = [&](const Stage &st, int s) __attribute__((always_inline)) {
+        store_q(st, s, std::integral_constant<int, 0>());
+        store_q(st, s, std::integral_constant<int, 1>());
+        store_q(st, s, std::integral_constant<int, 2>());
+        store_q(st, s, std::integral_constant<int, 3>());
     };
 
     f32x16_t acc[TM][TN];
@@ -360,34 +388,41 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
                                                                        0, 0, 0);
             }
     };
-    // Pipeline step kt computes on LDS buffer kt & 1.  The register stage then
-    // holds step kt + 1 (loaded one step earlier): its A half is staged into
-    // buffer (kt + 1) & 1 during the first k16 MFMA group and its W half
-    // during the second, and each half is reloaded with step kt + 2 right
-    // after it has been consumed, so global loads get a full step to land.
-    Stage st;
+    // Pipeline step kt computes on LDS buffer kt & 1.  Register stage `use`
+    // holds step kt + 1 (loaded during the previous step) and is staged into
+    // buffer (kt + 1) & 1, one quarter per k16 MFMA group (A's blocks in the
+    // first two groups, W's in the last two).  Step kt + 2 is loaded into
+    // `fill` before any MFMA, so the loads have the whole step to land, and
+    // moved into `use` at the end of the step.
+    Stage use, fill;
     auto step = [&](int kt, bool do_store, bool do_load) __attribute__((always_inline)) {
         const int cur = kt & 1;
+        if (do_load) {
+            load_part(fill, kt + 2, 0);
+            load_part(fill, kt + 2, 1);
+        }
         read_frags(cur, 0, af[0], bf[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-            if (ks == 0 && do_store) store_part(st, cur ^ 1, 0);
-            if (ks == 1 && do_load) load_part(st, kt + 2, 0);
-            if (ks == 1 && do_store) store_part(st, cur ^ 1, 1);
-            if (ks == 2 && do_load) load_part(st, kt + 2, 1);
+            if (do_store) {
+                if (ks == 0) store_q(use, cur ^ 1, std::integral_constant<int, 0>());
+                if (ks == 1) store_q(use, cur ^ 1, std::integral_constant<int, 1>());
+                if (ks == 2) store_q(use, cur ^ 1, std::integral_constant<int, 2>());
+                if (ks == 3) store_q(use, cur ^ 1, std::integral_constant<int, 3>());
+            }
             mfmas(af[ks & 1], bf[ks & 1]);
         }
+        if (do_load) use = fill;
     };
 
     if (KT > 0) {
-        load_part(st, 0, 0);
-        load_part(st, 0, 1);
-        store_part(st, 0, 0);
-        store_part(st, 0, 1);
+        load_part(use, 0, 0);
+        load_part(use, 0, 1);
+        store_all(use, 0);
         if (KT > 1) {
-            load_part(st, 1, 0);
-            load_part(st, 1, 1);
+            load_part(use, 1, 0);
+            load_part(use, 1, 1);
         }
     }
     __syncthreads();
