@@ -215,7 +215,7 @@ __device__ __forceinline__ void bf16_store(const Bf16Stage<Part<R, NT>::EPT> &st
 }
 
 // Fused prologue: quantize the staged BF16 values exactly as the standalone
-// quantizer does (same block_scale / quant_elem), then expand q * sigma.
+// quantizer does (same block_scale / quant8), then expand q * sigma.
 template <int R, int NT, int H = -1>
 __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, float alpha) {
     constexpr int EPT = Part<R, NT>::EPT;
@@ -232,13 +232,7 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
         const half2_t s2 = e4m3_to_f16x2_over256(bs.code);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = w[4 * c + i];
-                packed |= quant_elem(bf16_bits_to_f32(x & 0xFFFFu), bs.d) << (8 * i);
-                packed |= quant_elem(bf16_bits_to_f32(x >> 16), bs.d) << (8 * i + 4);
-            }
+            const uint32_t packed = quant8(&w[4 * c], bs.d);
             *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b + c)) = expand8(packed, s2);
         }
     }

@@ -96,6 +96,55 @@ __device__ __forceinline__ uint32_t quant_elem(float x, float d) {
     return e2m1_encode(v);
 }
 
+// Eq. 2 for 8 consecutive elements of one block: w[i] holds elements 2i
+// (low half) and 2i + 1 (high half) as BF16 bits; d = fl32(alpha * sigma).
+// Returns the 8 E2M1 codes packed, element i in nibble i.
+//
+// |x| / d is formed with Markstein's correction: r = RN(1/d) (one IEEE
+// division), q0 = RN(|x| r), then RN(q0 + (|x| - q0 d) r) with both steps as
+// fused multiply-adds equals RN(|x| / d) when d, 1/d and x stay clear of
+// underflow; d in [2^-100, 2^100] and |x| >= 2^-100 (or x == 0) qualify, and
+// anything else takes the IEEE division.  The magnitude is rounded to E2M1 by
+// the hardware FP32 -> FP4 convert (nearest-even with saturation; it agrees
+// with the compare ladder of e2m1_encode on every FP32 bit pattern) and the
+// sign is copied from x, which is the sign of x / d for d > 0.
+__device__ __forceinline__ uint32_t quant8(const uint32_t w[4], float d) {
+    uint32_t signs = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) signs |= (((w[i] >> 15) & 1u) << (8 * i + 3)) | (((w[i] >> 31) & 1u) << (8 * i + 7));
+    if (!(d > 0.0f)) return signs;  // zero divisor: signed zeros
+    // a BF16 magnitude m is "tiny" when 0 < m < 2^-100 (exponent field < 27)
+    bool fast = d >= 0x1p-100f && d <= 0x1p100f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        fast = fast && (lo - 1u >= (27u << 7) - 1u) && (hi - 1u >= (27u << 7) - 1u);
+    }
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[2 * i] = bf16_bits_to_f32(w[i] & 0x7FFFu);
+        a[2 * i + 1] = bf16_bits_to_f32((w[i] >> 16) & 0x7FFFu);
+    }
+    if (fast) {
+        const float r = div_rn(1.0f, d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q0 = a[i] * r;
+            a[i] = __builtin_fmaf(__builtin_fmaf(-q0, d, a[i]), r, q0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = div_rn(a[i], d);
+    }
+    uint32_t packed = 0;
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, a[0], a[1], 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, a[2], a[3], 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, a[4], a[5], 1.0f, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, a[6], a[7], 1.0f, 3);
+    return packed | signs;
+}
+
 // E2M1 code (4 bits) -> FP16 bits of the value q (exact).
 __device__ __forceinline__ uint32_t e2m1_to_f16_bits(uint32_t c) {
     uint32_t mag = c & 7u;

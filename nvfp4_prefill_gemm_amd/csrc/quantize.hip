@@ -40,12 +40,19 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(const uint16_t 
     const int64_t octs = cols >> 3;
     for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
         const uint4 *xr = reinterpret_cast<const uint4 *>(x + r * ld);
-        for (int64_t o = lane; o < octs; o += 64) {
-            uint4 v = load_nt16(xr + o);
-            m = __builtin_elementwise_max(m, abs_bf16x2(v.x));
-            m = __builtin_elementwise_max(m, abs_bf16x2(v.y));
-            m = __builtin_elementwise_max(m, abs_bf16x2(v.z));
-            m = __builtin_elementwise_max(m, abs_bf16x2(v.w));
+        constexpr int U = 4;  // 16-byte loads in flight per lane
+        for (int64_t o0 = lane; o0 < octs; o0 += 64 * U) {
+            uint4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = (o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
+                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
+                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
+                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
+            }
         }
     }
     uint32_t mm = max((uint32_t)m.x, (uint32_t)m.y) << 16;  // FP32 bits of the BF16 max
@@ -92,31 +99,31 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t octs = cols >> 3;  // 8-element groups per row; even, so pairs never straddle rows
+    constexpr int U = 4;             // 16-byte loads in flight per lane
     for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
         const uint4 *xr = reinterpret_cast<const uint4 *>(x + r * ld);
         uint32_t *cr = reinterpret_cast<uint32_t *>(codes + r * (cols >> 1));
         uint8_t *sr = scales + r * (cols >> 4);
-        for (int64_t o = lane; o < octs; o += 64) {
-            uint4 v = load_nt16(xr + o);
-            float f[8];
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int64_t o0 = lane; o0 < octs; o0 += 64 * U) {
+            uint4 v[U];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-                f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+            for (int u = 0; u < U; ++u)
+                v[u] = (o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = o0 + 64 * u;
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                uint32_t am = 0;  // bit pattern of max |x| over this lane's 8 elements
+#pragma unroll
+                for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+                // partner lane (o ^ 1) holds the other half of the 16-element block
+                const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
+                const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha);
+                if (o < octs) {
+                    cr[o] = quant8(w, bs.d);
+                    if ((o & 1) == 0) sr[o >> 1] = (uint8_t)bs.code;
+                }
             }
-            uint32_t am = 0;  // bit pattern of max |x| over this lane's 8 elements
-#pragma unroll
-            for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-            // partner lane (o ^ 1) holds the other half of the 16-element block
-            uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
-            float amax_b = bf16_bits_to_f32(max(am, other));
-            BlockScale bs = block_scale(amax_b, alpha);
-            uint32_t packed = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) packed |= quant_elem(f[i], bs.d) << (4 * i);
-            cr[o] = packed;
-            if ((o & 1) == 0) sr[o >> 1] = (uint8_t)bs.code;
         }
     }
 }
