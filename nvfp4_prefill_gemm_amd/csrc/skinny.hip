@@ -8,6 +8,9 @@
 // rows), keep U steps of loads in flight, and run 16x16x32 BF16 MFMAs with
 // X zero-padded to MG*16 rows.  The per-wave partial tiles are summed
 // through LDS at the end.
+#include <stdlib.h>
+#include <string.h>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -100,10 +103,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
     }
 }
 
-template <int MG, int NG>
+template <int MG, int NG, int WAVES, int U>
 hipError_t launch_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out, int out_type,
                       int64_t ld_out, hipStream_t s) {
-    constexpr int WAVES = 8, U = 4;
     const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (out_type == OUT_BF16)
@@ -122,11 +124,32 @@ __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, 
 
 }  // namespace
 
+// NVFP4_SKINNY_CFG=<waves>x<unroll> overrides the decode kernel shape (tuning knob).
+int skinny_cfg() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("NVFP4_SKINNY_CFG");
+        v = !e ? 0 : !strcmp(e, "8x4") ? 1 : !strcmp(e, "16x4") ? 2 : !strcmp(e, "16x8") ? 3 : !strcmp(e, "8x8") ? 4 : 0;
+    }
+    return v;
+}
+
+template <int MG, int NG>
+hipError_t launch_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out, int out_type,
+                     int64_t ld_out, hipStream_t s) {
+    switch (skinny_cfg()) {
+        case 1: return launch_cfg<MG, NG, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
+        case 3: return launch_cfg<MG, NG, 16, 8>(a, w, M, N, K, out, out_type, ld_out, s);
+        case 4: return launch_cfg<MG, NG, 8, 8>(a, w, M, N, K, out, out_type, ld_out, s);
+        default: return launch_cfg<MG, NG, 16, 4>(a, w, M, N, K, out, out_type, ld_out, s);
+    }
+}
+
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
                               int out_type, int64_t ld_out, hipStream_t s) {
-    if (M <= 16) return launch_cfg<1, 1>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (M <= 32) return launch_cfg<2, 2>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (M <= 64) return launch_cfg<4, 2>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (M <= 16) return launch_mg<1, 1>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (M <= 32) return launch_mg<2, 1>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (M <= 64) return launch_mg<4, 1>(a, w, M, N, K, out, out_type, ld_out, s);
     return hipErrorInvalidValue;
 }
 

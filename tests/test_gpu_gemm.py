@@ -234,3 +234,48 @@ def test_bf16_prefill_qwen3_8b_m8192_sampled(nv, oracle_mod, layer):
     ref = oracle_mod.bf16_gemm_pairs(a, wt, mi, ni)
     got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].float().cpu().numpy()
     parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, f"bf16 {name} sampled")
+
+
+@pytest.mark.parametrize("layer", range(4))
+def test_qwen3_32b_m16384_sampled(nv, oracle_mod, layer):
+    """Qwen3-32B prefill linears at 16384 tokens (dynamic-alpha activation
+    quantizer + NVFP4 GEMM, BF16 output); quantized activation bit-exact in
+    full, 4100 sampled outputs against the exact oracle."""
+    import torch
+
+    w = wl.WORKLOADS["qwen3_32b_m16384"]
+    name, K, N = w.linears[layer]
+    a, wt = wl.layer_inputs(w, layer)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    say("nvfp4 gemm qwen3-32b m16384", name, (w.M, N, K))
+    ac, asc, aal = nv.nvfp4_quantize(bf16_dev(a))
+    del a
+    assert np.array_equal(host(asc), A[1]) and np.array_equal(host(ac), A[0]) and host(aal)[0] == A[2]
+    wc, wsc, wal = _dev_operand(W)
+    y = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.bfloat16)
+    mi, ni = _sample_pairs(w.M, N, 4096, 300 + layer)
+    ref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
+    got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].float().cpu().numpy()
+    parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, f"32b {name} sampled")
+
+
+@pytest.mark.parametrize("M", [512, 2048, 32768])
+def test_phase_split_prefill_token_counts(nv, oracle_mod, M):
+    """NVFP4 prefill at the phase-split token counts (the 8192 case is covered
+    above), Qwen3-8B QKV and down projections, against the oracle."""
+    import torch
+
+    for layer in (0, 3):
+        name, K, N = wl.QWEN3_8B_LINEARS[layer]
+        a = wl.activations(M, K, wl.rng(wl.PHASE_SPLIT_CONFIG_ID, layer, 0))
+        wt = wl.weights(N, K, wl.rng(wl.PHASE_SPLIT_CONFIG_ID, layer, 1))
+        A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+        say("phase split prefill", name, (M, N, K))
+        ac, asc, aal = nv.nvfp4_quantize(bf16_dev(a))
+        assert np.array_equal(host(ac), A[0]) and np.array_equal(host(asc), A[1])
+        wc, wsc, wal = _dev_operand(W)
+        y = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.float32)
+        mi, ni = _sample_pairs(M, N, 2048, M + layer)
+        ref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
+        got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+        parity.assert_gemm_close(got, ref, parity.GEMM_TOL_F32, f"phase split {name} M={M}")
