@@ -12,6 +12,9 @@ Prefilling", Eq. 2 and Eq. 3; see ``nvfp4_oracle.c`` for the FP32 readings):
 * ``gemm_exact(...)``       -> float64 Y = xhatA @ xhatW^T, exact int64 sum
 * ``gemm_fp32(...)``        -> float32 Y from FP32 x_hat, products and k-ordered sums
 * ``bf16_gemm(a, w)``       -> float64 Y of the BF16 decode path
+* ``mx_quantize`` / ``mx_dequantize`` / ``mx_gemm``: MXFP4 (E2M1 + one E8M0
+  power-of-two scale per 32), the coarser format Section 3.3 contrasts with
+  NVFP4; rounding rule from the OCP MX v1.0 conversion (see nvfp4_oracle.c)
 
 Function-level pins live in ``tests/test_oracle_*.py``.
 """
@@ -68,6 +71,11 @@ def _load():
         "oracle_gemm_fp32": (I, [P, P, F, P, P, F, I64, I64, I64, P, I]),
         "oracle_bf16_gemm": (None, [P, P, I64, I64, I64, P, I]),
         "oracle_bf16_gemm_pairs": (None, [P, P, I64, P, P, I64, P, I]),
+        "oracle_e8m0_value": (ctypes.c_double, [I]),
+        "oracle_mx_quantize": (I, [P, I64, I64, I64, P, P, I]),
+        "oracle_mx_dequantize": (None, [P, P, I64, I64, P]),
+        "oracle_mx_gemm": (I, [P, P, P, P, I64, I64, I64, P, I]),
+        "oracle_mx_gemm_pairs": (I, [P, P, P, P, I64, P, P, I64, P, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -222,4 +230,51 @@ def bf16_gemm_pairs(a_bits, w_bits, mi, ni, nthreads: int = 0) -> np.ndarray:
     ni = _c(np.asarray(ni, dtype=np.int64), np.int64)
     out = np.empty(mi.size, dtype=np.float64)
     _load().oracle_bf16_gemm_pairs(_ptr(a), _ptr(w), a.shape[1], _ptr(mi), _ptr(ni), mi.size, _ptr(out), nthreads)
+    return out
+
+
+# --------------------------------------------------------------------------- MXFP4
+def e8m0_value(code: int) -> float:
+    return float(_load().oracle_e8m0_value(int(code)))
+
+
+def mx_quantize(x_bits: np.ndarray, nthreads: int = 0):
+    """BF16 bits [rows, cols] -> (codes [rows, cols/2], E8M0 scales [rows, cols/32])."""
+    x = _c(x_bits, np.uint16)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    scales = np.empty((rows, cols // 32), dtype=np.uint8)
+    if _load().oracle_mx_quantize(_ptr(x), rows, cols, cols, _ptr(codes), _ptr(scales), nthreads) != 0:
+        raise ValueError("oracle_mx_quantize: cols must be a multiple of 32")
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    rows, half = codes.shape
+    out = np.empty((rows, half * 2), dtype=np.float64)
+    _load().oracle_mx_dequantize(_ptr(codes), _ptr(scales), rows, half * 2, _ptr(out))
+    return out
+
+
+def mx_gemm(a_codes, a_scales, w_codes, w_scales, nthreads: int = 0) -> np.ndarray:
+    a_codes, a_scales = _c(a_codes, np.uint8), _c(a_scales, np.uint8)
+    w_codes, w_scales = _c(w_codes, np.uint8), _c(w_scales, np.uint8)
+    M, N, K = a_codes.shape[0], w_codes.shape[0], a_codes.shape[1] * 2
+    out = np.empty((M, N), dtype=np.float64)
+    if _load().oracle_mx_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K, _ptr(out),
+                              nthreads) != 0:
+        raise ValueError("oracle_mx_gemm: K must be a multiple of 32")
+    return out
+
+
+def mx_gemm_pairs(a_codes, a_scales, w_codes, w_scales, mi, ni, nthreads: int = 0) -> np.ndarray:
+    a_codes, a_scales = _c(a_codes, np.uint8), _c(a_scales, np.uint8)
+    w_codes, w_scales = _c(w_codes, np.uint8), _c(w_scales, np.uint8)
+    mi = _c(np.asarray(mi, dtype=np.int64), np.int64)
+    ni = _c(np.asarray(ni, dtype=np.int64), np.int64)
+    out = np.empty(mi.size, dtype=np.float64)
+    if _load().oracle_mx_gemm_pairs(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), a_codes.shape[1] * 2,
+                                    _ptr(mi), _ptr(ni), mi.size, _ptr(out), nthreads) != 0:
+        raise ValueError("oracle_mx_gemm_pairs: K must be a multiple of 32")
     return out

@@ -411,3 +411,130 @@ void oracle_bf16_gemm_pairs(const uint16_t *a, const uint16_t *w, int64_t K, con
     bf16_ctx g = {a, w, 0, K, out, mi, ni};
     parallel_rows(bf16_pairs, &g, npairs, nthreads);
 }
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4: E2M1 elements with one E8M0 (power-of-two) scale per 32 elements. */
+/* Mix-Quant Section 3.3 names MXFP4 as the coarser microscaling format with  */
+/* larger groups and power-of-two scales.  The pages give no rounding rule;   */
+/* the reading taken is the OCP Microscaling (MX) v1.0 conversion: shared     */
+/* exponent = floor(log2(max |x|)) - 2 (2 = largest E2M1 exponent), clamped   */
+/* to E8M0's [-127, 127]; an all-zero block takes the smallest scale 2^-127;  */
+/* elements are x / 2^shared rounded to E2M1 nearest-even with saturation.   */
+/* ------------------------------------------------------------------------ */
+
+/* E8M0 code -> value 2^(code - 127); code 255 is NaN. */
+double oracle_e8m0_value(int code) {
+    if ((code & 255) == 255) return NAN;
+    return ldexp(1.0, (code & 255) - 127);
+}
+
+typedef struct {
+    const uint16_t *x;
+    int64_t cols, ld;
+    uint8_t *codes, *scales;
+} mx_ctx;
+
+static void mx_rows(void *p, int64_t r0, int64_t r1) {
+    mx_ctx *q = (mx_ctx *)p;
+    const int64_t nb = q->cols / 32;
+    for (int64_t r = r0; r < r1; ++r) {
+        const uint16_t *xr = q->x + r * q->ld;
+        for (int64_t b = 0; b < nb; ++b) {
+            double v[32], amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                v[i] = (double)bf16_to_float(xr[b * 32 + i]);
+                if (fabs(v[i]) > amax) amax = fabs(v[i]);
+            }
+            int shared = -127;
+            if (amax > 0.0) {
+                int e;
+                frexp(amax, &e);   /* amax = m * 2^e, m in [0.5, 1): floor(log2 amax) = e - 1 */
+                shared = (e - 1) - 2;
+                if (shared < -127) shared = -127;
+                if (shared > 127) shared = 127;
+            }
+            q->scales[r * nb + b] = (uint8_t)(shared + 127);
+            uint8_t codes[32];
+            for (int i = 0; i < 32; ++i) {
+                double y = ldexp(v[i], -shared); /* exact */
+                codes[i] = (uint8_t)oracle_e2m1_encode((float)y);
+            }
+            for (int j = 0; j < 16; ++j)
+                q->codes[r * (q->cols / 2) + b * 16 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+    }
+}
+
+/* x: BF16 bits [rows, ld]; codes [rows, cols/2]; scales [rows, cols/32] E8M0.
+ * Returns 0, or -1 when cols % 32 != 0 or ld < cols.                         */
+int oracle_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                       uint8_t *scales, int nthreads) {
+    if (cols % 32 != 0 || ld < cols || rows < 0) return -1;
+    tables();
+    mx_ctx q = {x, cols, ld, codes, scales};
+    parallel_rows(mx_rows, &q, rows, nthreads);
+    return 0;
+}
+
+/* x_hat = 2^shared * q, float64 (exact). */
+void oracle_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                          double *out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t byte = codes[r * (cols / 2) + c / 2];
+            int code = (c & 1) ? (byte >> 4) : (byte & 15);
+            out[r * cols + c] = oracle_e8m0_value(scales[r * (cols / 32) + c / 32]) * oracle_e2m1_value(code);
+        }
+}
+
+/* Y[m,n] = sum_b 2^(sA[m,b] + sW[n,b]) * sum_{k in b} qA qW.  Each block sum is
+ * an exact integer (in quarter units) times an exact power of two; the block
+ * terms are added in float64 in increasing b.                                */
+typedef struct {
+    const uint8_t *ac, *as, *wc, *ws;
+    int64_t N, K;
+    double *out;
+    const int64_t *mi, *ni;
+} mxg_ctx;
+static double mx_dot(const mxg_ctx *g, int64_t m, int64_t n) {
+    const int64_t nb = g->K / 32;
+    double acc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t p = 0;
+        for (int i = 0; i < 32; ++i) {
+            int64_t k = b * 32 + i;
+            uint8_t ba = g->ac[m * (g->K / 2) + k / 2], bw = g->wc[n * (g->K / 2) + k / 2];
+            int ca = (k & 1) ? (ba >> 4) : (ba & 15), cw = (k & 1) ? (bw >> 4) : (bw & 15);
+            p += (int64_t)lrint(2.0 * oracle_e2m1_value(ca)) * (int64_t)lrint(2.0 * oracle_e2m1_value(cw));
+        }
+        int e = ((int)g->as[m * nb + b] - 127) + ((int)g->ws[n * nb + b] - 127) - 2;
+        acc += ldexp((double)p, e);
+    }
+    return acc;
+}
+static void mxg_rows(void *p, int64_t r0, int64_t r1) {
+    mxg_ctx *g = (mxg_ctx *)p;
+    for (int64_t m = r0; m < r1; ++m)
+        for (int64_t n = 0; n < g->N; ++n) g->out[m * g->N + n] = mx_dot(g, m, n);
+}
+static void mxg_pairs(void *p, int64_t i0, int64_t i1) {
+    mxg_ctx *g = (mxg_ctx *)p;
+    for (int64_t i = i0; i < i1; ++i) g->out[i] = mx_dot(g, g->mi[i], g->ni[i]);
+}
+int oracle_mx_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+                   const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, double *out, int nthreads) {
+    if (K % 32 != 0) return -1;
+    tables();
+    mxg_ctx g = {a_codes, a_scales, w_codes, w_scales, N, K, out, NULL, NULL};
+    parallel_rows(mxg_rows, &g, M, nthreads);
+    return 0;
+}
+int oracle_mx_gemm_pairs(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+                         const uint8_t *w_scales, int64_t K, const int64_t *mi, const int64_t *ni,
+                         int64_t npairs, double *out, int nthreads) {
+    if (K % 32 != 0) return -1;
+    tables();
+    mxg_ctx g = {a_codes, a_scales, w_codes, w_scales, 0, K, out, mi, ni};
+    parallel_rows(mxg_pairs, &g, npairs, nthreads);
+    return 0;
+}
