@@ -125,6 +125,31 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
 int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int64_t K, void *out,
               int out_dtype, int64_t ld_out, void *stream);
 
+/*
+ * MXFP4 (Mix-Quant Section 3.3 names it as the coarser microscaling format
+ * with larger groups and power-of-two scales): E2M1 codes as above and one
+ * E8M0 scale byte (value 2^(code - 127)) per 32 consecutive elements, no
+ * tensor scale.  Rounding follows the OCP MX v1.0 conversion: shared
+ * exponent floor(log2(max |x|)) - 2 clamped to [-127, 127] (-127 for an
+ * all-zero block), elements x / 2^shared to E2M1 nearest-even, saturating.
+ *   x_bf16 [rows, ld_x] BF16 (16-byte aligned, ld_x % 8 == 0), cols % 32 == 0
+ *   codes  [rows, cols/2] uint8 out (16-byte aligned)
+ *   scales [rows, cols/32] uint8 out (E8M0)
+ */
+int mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                   uint8_t *scales, void *stream);
+
+/*
+ * MXFP4 x MXFP4 GEMM on gfx950's block-scaled FP4 MFMAs:
+ *   Y[m, n] = sum_b 2^(sA[m,b] + sW[n,b]) sum_{k in b} qA[m,k] qW[n,k]
+ *   a_codes [M, K/2], a_scales [M, K/32], w_codes [N, K/2], w_scales [N, K/32]
+ *   K % 32 == 0; code arrays 16-byte aligned, scale arrays 8-byte aligned
+ *   out [M, ld_out] FP32 or BF16 (nearest-even), FP32 accumulation.
+ */
+int mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+               const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *out, int out_dtype,
+               int64_t ld_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,8 @@ _SIGNATURES = {
     "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quant_gemm": (_I, [_P, _I64, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "bf16_gemm": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
+    "mxfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "mxfp4_gemm": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
 }
 
 
@@ -181,4 +183,37 @@ def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     rc = lib().bf16_gemm(_ptr(a), _ptr(w), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _stream(stream))
     _check("bf16_gemm", rc)
+    return out
+
+
+def mxfp4_quantize(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                   stream=None):
+    """BF16 [rows, cols] -> MXFP4 (codes uint8 [rows, cols/2], E8M0 scales uint8 [rows, cols/32])."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D row-major tensor")
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    rc = lib().mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(codes), _ptr(scales), _stream(stream))
+    _check("mxfp4_quantize", rc)
+    return codes, scales
+
+
+def mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+               stream=None) -> torch.Tensor:
+    """Y [M, N] = dequant(A) @ dequant(W)^T from MXFP4 operands."""
+    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
+        _dev(t, n, torch.uint8)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("A and W disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    rc = lib().mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K, _ptr(out),
+                          _OUT[out.dtype], out.stride(0), _stream(stream))
+    _check("mxfp4_gemm", rc)
     return out

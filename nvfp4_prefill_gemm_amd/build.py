@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ("api.hip", "quantize.hip", "gemm.hip", "skinny.hip")
+SOURCES = ("api.hip", "quantize.hip", "gemm.hip", "skinny.hip", "mxfp4.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -171,4 +171,36 @@ int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int6
                       "bf16 gemm kernel");
 }
 
+int mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes, uint8_t *scales,
+                   void *stream) {
+    const char *fn = "mxfp4_quantize";
+    if (rows < 0 || cols < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (cols % 32 != 0) return fail(NVFP4_EINVAL, "%s: cols (%lld) must be a multiple of 32", fn, (long long)cols);
+    if (rows == 0 || cols == 0) return ok();
+    if (!x_bf16 || !codes || !scales) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
+    if (ld_x < cols || ld_x % 8 != 0) return fail(NVFP4_EINVAL, "%s: ld_x must be >= cols and a multiple of 8", fn);
+    if (!aligned(x_bf16, 16) || !aligned(codes, 16)) return fail(NVFP4_EINVAL, "%s: x and codes must be 16-byte aligned", fn);
+    return hip_status(nvfp4::launch_mx_quantize((const uint16_t *)x_bf16, rows, cols, ld_x, codes, scales,
+                                                as_stream(stream)),
+                      "mx quantize kernel");
+}
+
+int mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes, const uint8_t *w_scales,
+               int64_t M, int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out, void *stream) {
+    const char *fn = "mxfp4_gemm";
+    if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (K % 32 != 0) return fail(NVFP4_EINVAL, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    int rc = check_out(out, out_dtype, N, ld_out, fn);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    const int esz = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
+    if (!a_codes || !a_scales || !w_codes || !w_scales) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
+    if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 8) || !aligned(w_scales, 8))
+        return fail(NVFP4_EINVAL, "%s: codes must be 16-byte and scales 8-byte aligned", fn);
+    return hip_status(nvfp4::launch_mx_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, out, out_dtype, ld_out, s),
+                      "mx gemm kernel");
+}
+
 }  // extern "C"

@@ -31,6 +31,7 @@
 
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
+#include "tiling.hpp"
 
 namespace nvfp4 {
 
@@ -50,19 +51,7 @@ using BigTile = TileCfg<256, 256, 2, 2, 1>;   // 4 waves of 128 x 128
 using BigTile8 = TileCfg<256, 256, 2, 4, 1>;  // 8 waves of 128 x 64
 using SmallTile = TileCfg<128, 128, 2, 2, 2>; // 4 waves of 64 x 64
 
-// LDS tile layout: row-major rows of 64 halves (eight 16-byte chunks); chunk c
-// of row r sits in slot c ^ f(r).  Measured on gfx950, 16-byte LDS reads are
-// served 16 lanes per cycle across 64 banks (two 128-byte rows) and 16-byte
-// writes 8 lanes per cycle across 32 banks (one row).  An MFMA operand read
-// touches 16 consecutive rows (16-aligned) at one chunk, so f must be one-to-
-// one on the even rows and on the odd rows of each 16-row group; a staging
-// write touches 4 consecutive rows (4-aligned) at chunks {k, k + 4}, so f's
-// low two bits must differ across each 4-row group.  f(r) = s((r >> 1) & 7)
-// ^ (r & 1), with s swapping bits 0 and 1, satisfies both.
-__device__ __forceinline__ int lds_swz(int row) {
-    const int m = (row >> 1) & 7;
-    return (((m & 1) << 1) | ((m >> 1) & 1) | (m & 4)) ^ (row & 1);
-}
+// LDS tile layout: rows of 64 halves (eight 16-byte chunks), swizzled by lds_swz.
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ lds_swz(row)) << 3); }
 
 struct GemmArgs {
@@ -240,24 +229,6 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
 
 // ---------------------------------------------------------------- kernel
 enum Kind { KIND_NVFP4 = 0, KIND_FUSED = 1, KIND_BF16 = 2 };
-
-template <class C>
-__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int &tm, int &tn) {
-    const int num_tm = (int)((M + C::BM - 1) / C::BM), num_tn = (int)((N + C::BN - 1) / C::BN);
-    const int nb = gridDim.x;
-    int bid = blockIdx.x;
-    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-    // contiguous range of logical tiles so neighbouring tiles share its L2.
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-    constexpr int G = 8;  // tiles along M per group: W tiles are reused across it
-    const int per_group = G * num_tn;
-    const int group = bid / per_group;
-    const int first_tm = group * G;
-    const int gsize = min(num_tm - first_tm, G);
-    const int in = bid % per_group;
-    tm = first_tm + in % gsize;
-    tn = in / gsize;
-}
 
 // Register stage of one pipeline step, per operand kind: A then W.
 template <class SA, class SW>
@@ -464,7 +435,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_kernel(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     lds_t *lds = reinterpret_cast<lds_t *>(smem);
     int tm, tn;
-    tile_coords<C>(g.M, g.N, tm, tn);
+    tile_coords<C::BM, C::BN>(g.M, g.N, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const bool full = m0 + C::BM <= g.M && n0 + C::BN <= g.N && (g.K & (BK - 1)) == 0;
     if (full)

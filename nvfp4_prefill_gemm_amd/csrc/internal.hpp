@@ -41,6 +41,13 @@ hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, i
 // Largest M routed to the skinny decode kernel by bf16_gemm.
 constexpr int64_t kSkinnyMaxM = 64;
 
+hipError_t launch_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                              uint8_t *scales, hipStream_t s);
+
+hipError_t launch_mx_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+                          const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *out, int out_type,
+                          int64_t ld_out, hipStream_t s);
+
 hipError_t launch_fill_zero(void *out, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s);
 
 }  // namespace nvfp4
