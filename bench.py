@@ -301,8 +301,31 @@ def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
     out["mxfp4_gemm_tflops"] = {L["name"]: round(wl.flops(M, L["N"], L["K"]) / (mt.total_ms(("mxgemm", L["name"])) / reps
                                                                               * 1e-3) / 1e12, 1) for L in layers}
 
-    # BF16 decode GEMMs on the same weights; two rotating weight copies so the
-    # 256 MB Infinity Cache cannot hold a step's weights
+    # Decode steps (one token batch through the four layers) are replayed from
+    # HIP graphs, as a serving loop runs them: per-call host overhead would
+    # otherwise exceed these kernels' GPU time.  Weights rotate over copies
+    # that together exceed the 256 MB Infinity Cache.
+    def graph_us(step, copies, n):
+        graphs = []
+        for c in range(copies):
+            step(c)  # warm-up: first-launch attribute setup stays out of the graph
+        torch.cuda.synchronize()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        s.record()
+        for r in range(n):
+            graphs[r % copies].replay()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n * 1e3
+
+    # BF16 decode GEMMs (the method's decode precision): two weight copies
     copies = [[L["w_bf16"] for L in layers], [L["w_bf16"].clone() for L in layers]]
     decode = {}
     for Md in wl.PHASE_SPLIT_DECODE_M:
@@ -312,21 +335,42 @@ def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
         def dec_step(c):
             for i, L in enumerate(layers):
                 nv.bf16_gemm(xs[i], copies[c][i], out=ys[i])
-        for c in (0, 1):
-            dec_step(c)
-        torch.cuda.synchronize()
-        n = 10
-        s.record()
-        for r in range(n):
-            dec_step(r & 1)
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / n
+        us = graph_us(dec_step, 2, 20)
         nbytes = sum(2 * L["N"] * L["K"] + 2 * Md * L["K"] + 2 * Md * L["N"] for L in layers)
-        decode[str(Md)] = {"us_per_step": round(ms * 1e3, 1), "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                           "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 3)}
+        decode[str(Md)] = {"us_per_step": round(us, 1), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                           "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3)}
     out["decode_bf16"] = decode
     del copies
+
+    # NVFP4 x NVFP4 decode (the uniform-NVFP4 / FP4-decode ablation variants):
+    # dynamic-alpha activation quantizer + decode GEMM per layer; a step's
+    # NVFP4 weights (109 MB) fit the Infinity Cache, so four copies rotate.
+    wq = [[(L["wc"], L["ws"], L["wa"]) for L in layers]]
+    for _ in range(3):
+        wq.append([(L["wc"].clone(), L["ws"].clone(), L["wa"]) for L in layers])
+    dec4 = {}
+    for Md in wl.PHASE_SPLIT_DECODE_M:
+        xs = [torch.randn((Md, L["K"]), device=dev).to(torch.bfloat16) for L in layers]
+        ys = [torch.empty((Md, L["N"]), dtype=torch.bfloat16, device=dev) for L in layers]
+        qa = [(torch.empty((Md, L["K"] // 2), dtype=torch.uint8, device=dev),
+               torch.empty((Md, L["K"] // 16), dtype=torch.uint8, device=dev),
+               torch.empty(1, dtype=torch.float32, device=dev),
+               torch.empty(max(nv.quantize_workspace_size(Md, L["K"]), 4), dtype=torch.uint8, device=dev))
+              for L in layers]
+
+        def dec4_step(c):
+            for i, L in enumerate(layers):
+                ac, asc, aal, wsb = qa[i]
+                nv.nvfp4_quantize(xs[i], ac, asc, aal, workspace=wsb)
+                nv.nvfp4_gemm(ac, asc, aal, *wq[c][i], out=ys[i])
+        us = graph_us(dec4_step, 4, 20)
+        nbytes = sum(L["N"] * L["K"] * 9 // 16 + 2 * Md * L["K"] + Md * L["K"] * 9 // 16 + 2 * Md * L["N"]
+                     for L in layers)
+        dec4[str(Md)] = {"us_per_step": round(us, 1), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3),
+                         "speedup_vs_bf16_decode": round(decode[str(Md)]["us_per_step"] / us, 3)}
+    out["decode_nvfp4"] = dec4
+    del wq
     return out
 
 

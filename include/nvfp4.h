@@ -88,9 +88,12 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
  *   Y[m, n] = sum_k xhatA[m, k] * xhatW[n, k],   xhat = alpha * sigma * q (Eq. 2)
  *   a_codes [M, K/2], a_scales [M, K/16], a_alpha float[1]   (activations)
  *   w_codes [N, K/2], w_scales [N, K/16], w_alpha float[1]   (weights)
- *   K % 16 == 0; M, N >= 0; code arrays 16-byte aligned
+ *   K % 16 == 0; M, N >= 0; code arrays 16-byte aligned, scale arrays 4-byte aligned
  *   out [M, ld_out] FP32 (NVFP4_OUT_F32) or BF16 (NVFP4_OUT_BF16, nearest-even),
  *   ld_out >= N.  Accumulation is FP32; each product q*sigma is exact.
+ * At decode shapes (M <= 64, K % 32 == 0; the uniform-NVFP4 and FP4-decode
+ * variants of Mix-Quant Section 4) a split-K kernel streams the weights;
+ * otherwise a tile kernel runs.  Both sum in FP32 but in different orders.
  */
 int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
@@ -103,7 +106,9 @@ size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t K);
  * Fused prefill linear: BF16 activations are quantized to NVFP4 inside the
  * GEMM's operand staging (Mix-Quant Section 3.3: quantization, dequantization
  * and the matrix product fused by the backend).  The result equals
- * nvfp4_quantize followed by nvfp4_gemm; no codes or scales are written.
+ * nvfp4_quantize followed by nvfp4_gemm bit for bit whenever nvfp4_gemm takes
+ * its tile kernel (M > 64 or K % 32 != 0; at decode shapes it sums in another
+ * order); no codes or scales are written.
  *   x_bf16 [M, ld_x] BF16 (16-byte aligned, ld_x % 8 == 0), K % 16 == 0
  *   a_alpha float[1]: written (dynamic) or read (static) as in nvfp4_quantize
  *   weights, out, out_dtype, ld_out as in nvfp4_gemm

@@ -45,6 +45,7 @@ int check_out(const void *out, int out_dtype, int64_t N, int64_t ld_out, const c
 int check_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *alpha, const char *which, const char *fn) {
     if (!codes || !scales || !alpha) return fail(NVFP4_EINVAL, "%s: %s codes, scales and alpha must be non-null", fn, which);
     if (!aligned(codes, 16)) return fail(NVFP4_EINVAL, "%s: %s codes must be 16-byte aligned", fn, which);
+    if (!aligned(scales, 4)) return fail(NVFP4_EINVAL, "%s: %s scales must be 4-byte aligned", fn, which);
     return NVFP4_OK;
 }
 
@@ -106,6 +107,10 @@ int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_a
     if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
     if ((rc = check_nvfp4(a_codes, a_scales, a_alpha, "A", fn))) return rc;
     if ((rc = check_nvfp4(w_codes, w_scales, w_alpha, "W", fn))) return rc;
+    if (M <= nvfp4::kSkinnyMaxM && K % 32 == 0)
+        return hip_status(nvfp4::launch_skinny_nvfp4(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K,
+                                                     out, out_dtype, ld_out, s),
+                          "nvfp4 decode kernel");
     return hip_status(nvfp4::launch_gemm_nvfp4(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out,
                                                out_dtype, ld_out, s),
                       "nvfp4 gemm kernel");

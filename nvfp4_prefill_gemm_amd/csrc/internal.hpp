@@ -38,7 +38,15 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K,
                               void *out, int out_type, int64_t ld_out, hipStream_t s);
 
-// Largest M routed to the skinny decode kernel by bf16_gemm.
+// NVFP4 x NVFP4 at decode shapes: M <= kSkinnyMaxM, K % 32 == 0, codes
+// 16-byte and scales 2-byte aligned (nvfp4_gemm checks and otherwise uses the
+// tile kernel).
+hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                               const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                               int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                               hipStream_t s);
+
+// Largest M routed to the skinny decode kernels by bf16_gemm and nvfp4_gemm.
 constexpr int64_t kSkinnyMaxM = 64;
 
 hipError_t launch_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,

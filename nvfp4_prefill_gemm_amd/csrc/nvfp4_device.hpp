@@ -145,14 +145,26 @@ __device__ __forceinline__ uint32_t quant8(const uint32_t w[4], float d) {
     return packed | signs;
 }
 
-// E2M1 code (4 bits) -> FP16 bits of the value q (exact).
-__device__ __forceinline__ uint32_t e2m1_to_f16_bits(uint32_t c) {
-    uint32_t mag = c & 7u;
-    uint32_t b = mag >= 2u ? (mag + 28u) << 9 : (mag ? 0x3800u : 0u);
-    return b | ((c & 8u) << 12);
+// 8 E2M1 codes (one 32-bit word, element 0 in the low nibble) times sigma ->
+// 8 FP16 values, exactly.  The hardware converts FP4 pairs to FP16 with a
+// power-of-two scale of 2^8; sig2 holds sigma * 2^-8 in both halves, and one
+// packed FP16 multiply forms q * sigma.  Every factor is exact in FP16 and so
+// is the product (q * sigma has <= 6 significant bits, in [2^-10, 2688]).
+__device__ __forceinline__ half8_t expand8(uint32_t w, half2_t sig2) {
+    half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * sig2;
+    half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * sig2;
+    half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * sig2;
+    half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * sig2;
+    return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// FP32 value of an E4M3 code as FP16 (exact for every finite E4M3 value).
-__device__ __forceinline__ half_t e4m3_to_f16(uint32_t c) { return (half_t)e4m3_decode(c); }
+// sigma * 2^-8 as FP16, in both halves, from an E4M3 code (sign clear).
+// Read as FP16 bits, code << 7 lines E4M3's exponent field up with FP16's
+// (bias 15 = 7 + 8) and its three mantissa bits with FP16's top three, and
+// E4M3 subnormals m * 2^-9 land on FP16 subnormals m * 2^-17; so the value is
+// exactly sigma * 2^-8 for every finite code, with no branch.
+__device__ __forceinline__ half2_t e4m3_to_f16x2_over256(uint32_t c) {
+    return __builtin_bit_cast(half2_t, (c << 7) | (c << 23));
+}
 
 }  // namespace nvfp4

@@ -18,6 +18,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxParts = 1024;
+// Work item of both passes: kSeg 8-element groups (2048 elements) of one row,
+// kU 16-byte loads in flight per lane; short rows give one item each, long
+// rows several, so small batches still spread over many waves.
+constexpr int kU = 4;
+constexpr int64_t kSeg = 64 * kU;
 
 typedef __attribute__((ext_vector_type(2))) unsigned short ushort2_t;
 
@@ -38,21 +43,21 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(const uint16_t 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     ushort2_t m = {0, 0};
     const int64_t octs = cols >> 3;
-    for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
+    const int64_t nseg = (octs + kSeg - 1) / kSeg;
+    const int64_t items = rows * nseg;
+    for (int64_t it = (int64_t)blockIdx.x * kWaves + wave; it < items; it += (int64_t)gridDim.x * kWaves) {
+        const int64_t r = it / nseg, o0 = (it - r * nseg) * kSeg + lane;
         const uint4 *xr = reinterpret_cast<const uint4 *>(x + r * ld);
-        constexpr int U = 4;  // 16-byte loads in flight per lane
-        for (int64_t o0 = lane; o0 < octs; o0 += 64 * U) {
-            uint4 v[U];
+        uint4 v[kU];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                v[u] = (o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kU; ++u)
+            v[u] = (o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
-                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
-                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
-                m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
-            }
+        for (int u = 0; u < kU; ++u) {
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
         }
     }
     uint32_t mm = max((uint32_t)m.x, (uint32_t)m.y) << 16;  // FP32 bits of the BF16 max
@@ -90,6 +95,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
                                                             int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
                                                             uint8_t *__restrict__ scales, float *__restrict__ alpha_io,
                                                             const uint32_t *__restrict__ partials, int nparts) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t octs = cols >> 3;  // 8-element groups per row; even, so pairs never straddle rows
+    const int64_t nseg = (octs + kSeg - 1) / kSeg;
+    const int64_t items = rows * nseg, stride = (int64_t)gridDim.x * kWaves;
+    auto load_item = [&](int64_t it, uint4 *v) __attribute__((always_inline)) {
+        const int64_t r = it / nseg, o0 = (it - r * nseg) * kSeg + lane;
+        const uint4 *xr = reinterpret_cast<const uint4 *>(x + r * ld);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            v[u] = (it < items && o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
+    };
+    // the first item's loads are issued before the tensor scale is reduced
+    int64_t it = (int64_t)blockIdx.x * kWaves + wave;
+    uint4 v[kU];
+    load_item(it, v);
     float alpha;
     if (kDynamic) {
         alpha = alpha_from_partials(partials, nparts);
@@ -97,39 +117,33 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     } else {
         alpha = *alpha_io;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t octs = cols >> 3;  // 8-element groups per row; even, so pairs never straddle rows
-    constexpr int U = 4;             // 16-byte loads in flight per lane
-    for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
-        const uint4 *xr = reinterpret_cast<const uint4 *>(x + r * ld);
+    for (; it < items; it += stride) {
+        if (it != (int64_t)blockIdx.x * kWaves + wave) load_item(it, v);
+        const int64_t r = it / nseg, o0 = (it - r * nseg) * kSeg + lane;
         uint32_t *cr = reinterpret_cast<uint32_t *>(codes + r * (cols >> 1));
         uint8_t *sr = scales + r * (cols >> 4);
-        for (int64_t o0 = lane; o0 < octs; o0 += 64 * U) {
-            uint4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                v[u] = (o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t o = o0 + 64 * u;
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t am = 0;  // bit pattern of max |x| over this lane's 8 elements
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t o = o0 + 64 * u;
-                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-                uint32_t am = 0;  // bit pattern of max |x| over this lane's 8 elements
-#pragma unroll
-                for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-                // partner lane (o ^ 1) holds the other half of the 16-element block
-                const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
-                const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha);
-                if (o < octs) {
-                    cr[o] = quant8(w, bs.d);
-                    if ((o & 1) == 0) sr[o >> 1] = (uint8_t)bs.code;
-                }
+            for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+            // partner lane (o ^ 1) holds the other half of the 16-element block
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
+            const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha);
+            if (o < octs) {
+                cr[o] = quant8(w, bs.d);
+                if ((o & 1) == 0) sr[o >> 1] = (uint8_t)bs.code;
             }
         }
     }
 }
 
-int quant_grid(int64_t rows) {
-    int64_t g = (rows + kWaves - 1) / kWaves;
+int64_t quant_items(int64_t rows, int64_t cols) { return rows * (((cols >> 3) + kSeg - 1) / kSeg); }
+
+int quant_grid(int64_t rows, int64_t cols) {
+    int64_t g = (quant_items(rows, cols) + kWaves - 1) / kWaves;
     if (g > 65536) g = 65536;
     return (int)(g < 1 ? 1 : g);
 }
@@ -137,8 +151,7 @@ int quant_grid(int64_t rows) {
 }  // namespace
 
 int amax_parts(int64_t rows, int64_t cols) {
-    (void)cols;
-    int64_t g = (rows + kWaves - 1) / kWaves;
+    int64_t g = (quant_items(rows, cols) + kWaves - 1) / kWaves;
     if (g > kMaxParts) g = kMaxParts;
     return (int)(g < 1 ? 1 : g);
 }
@@ -152,7 +165,7 @@ hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, i
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials, int nparts,
                            hipStream_t s) {
-    dim3 grid(quant_grid(rows)), block(kThreads);
+    dim3 grid(quant_grid(rows, cols)), block(kThreads);
     if (dynamic)
         hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, s, x, rows, cols, ld, codes, scales, alpha,
                            partials, nparts);

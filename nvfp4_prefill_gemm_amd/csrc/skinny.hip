@@ -1,6 +1,6 @@
-// BF16 decode GEMM for small batches (M <= 64): Y[M, N] = X[M, K] * W[N, K]^T.
+// Decode-shape GEMMs for small batches (M <= 64): Y[M, N] = X[M, K] * W[N, K]^T.
 //
-// Decode keeps the original BF16 weights (Mix-Quant Section 3.3,
+// BF16: decode keeps the original BF16 weights (Mix-Quant Section 3.3,
 // "Prefill-Decode Disaggregation Deployment") and is bound by streaming W
 // from HBM: 2*N*K bytes against 2*M*N*K flops.  Each workgroup owns a strip
 // of NG*16 weight rows; its waves split K in 32-wide steps (interleaved, so
@@ -8,6 +8,16 @@
 // rows), keep U steps of loads in flight, and run 16x16x32 BF16 MFMAs with
 // X zero-padded to MG*16 rows.  The per-wave partial tiles are summed
 // through LDS at the end.
+//
+// NVFP4 (both operands E2M1 + E4M3 per 16, the uniform-NVFP4 and
+// FP4-decode variants of Mix-Quant's ablations, Section 4): the same split-K
+// layout streams 0.5625 bytes per weight instead of 2.  A lane's 16-byte code
+// load covers 32 consecutive K; the four 16x16x32 MFMA sub-steps of a
+// 128-wide K chunk take its four 8-code words, so sub-step t of lane group g
+// holds K = 128c + 32g + 8t + i on both operands (the same permutation of K
+// for A and W, which leaves the dot product unchanged).  Codes are expanded
+// exactly to q * sigma in FP16 in registers; alpha_A * alpha_W is applied in
+// the epilogue as in the prefill GEMM.
 #include <stdlib.h>
 #include <string.h>
 
@@ -20,11 +30,43 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f4_t;
 
+// Sum the per-wave 16x16 partial tiles of a workgroup through LDS, one
+// (row group, column group) tile at a time, and store y = (sum * sa) * sw:
+// out[m = i*16 + (l>>4)*4 + r][n = n0 + j*16 + (l & 15)].
+template <int MG, int NG, int WAVES, bool kOutBf16>
+__device__ __forceinline__ void tile_reduce(const f4_t (&acc)[MG][NG], float sa, float sw, int64_t M, int64_t N,
+                                            int64_t n0, void *__restrict__ out, int64_t ld_out) {
+    __shared__ float red[WAVES][64][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < MG; ++i)
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            if (i + j > 0) __syncthreads();  // previous tile consumed
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][lane][r] = acc[i][j][r];
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < 256; idx += WAVES * 64) {
+                const int r = idx & 3, l = idx >> 2;
+                float s = 0.f;
+#pragma unroll
+                for (int v = 0; v < WAVES; ++v) s += red[v][l][r];
+                const float y = (s * sa) * sw;
+                const int64_t m = i * 16 + (l >> 4) * 4 + r, n = n0 + j * 16 + (l & 15);
+                if (m < M && n < N) {
+                    if (kOutBf16)
+                        reinterpret_cast<uint16_t *>(out)[m * ld_out + n] = (uint16_t)f32_to_bf16_bits(y);
+                    else
+                        reinterpret_cast<float *>(out)[m * ld_out + n] = y;
+                }
+            }
+        }
+}
+
 template <int MG, int NG, int WAVES, int U, bool kOutBf16>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                             int64_t M, int64_t N, int64_t K, void *__restrict__ out,
                                                             int64_t ld_out) {
-    __shared__ float red[WAVES][MG][NG][64][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int kq = (lane >> 4) * 8;
@@ -78,29 +120,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
                                                                         acc[i][j], 0, 0, 0);
     }
 
-#pragma unroll
-    for (int i = 0; i < MG; ++i)
-#pragma unroll
-        for (int j = 0; j < NG; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][i][j][lane][r] = acc[i][j][r];
-    __syncthreads();
-
-    // out[m = i*16 + (l>>4)*4 + r][n = n0 + j*16 + (l & 15)]
-    constexpr int TOTAL = MG * NG * 64 * 4;
-    for (int idx = threadIdx.x; idx < TOTAL; idx += WAVES * 64) {
-        const int r = idx & 3, l = (idx >> 2) & 63, j = (idx >> 8) % NG, i = (idx >> 8) / NG;
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < WAVES; ++v) s += red[v][i][j][l][r];
-        const int64_t m = i * 16 + (l >> 4) * 4 + r, n = n0 + j * 16 + (l & 15);
-        if (m < M && n < N) {
-            if (kOutBf16)
-                reinterpret_cast<uint16_t *>(out)[m * ld_out + n] = (uint16_t)f32_to_bf16_bits(s);
-            else
-                reinterpret_cast<float *>(out)[m * ld_out + n] = s;
-        }
-    }
+    tile_reduce<MG, NG, WAVES, kOutBf16>(acc, 1.0f, 1.0f, M, N, n0, out, ld_out);
 }
 
 template <int MG, int NG, int WAVES, int U>
@@ -117,6 +137,104 @@ hipError_t launch_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N
     return hipGetLastError();
 }
 
+// NVFP4 x NVFP4, M <= MG*16, NG*16 weight rows per workgroup, K % 32 == 0,
+// 16-byte aligned codes and 4-byte aligned scales.
+template <int MG, int NG, int WAVES, int U, bool kOutBf16>
+__global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ a_alpha,
+    const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, const float *__restrict__ w_alpha, int64_t M,
+    int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
+    const int64_t cb = K >> 1, sb = K >> 4;  // code and scale bytes per row
+    const int64_t KC = (K + 127) >> 7;       // 128-wide K chunks
+    const int kg = (lane >> 4) * 32;         // this lane group's K offset in a chunk
+
+    f4_t acc[MG][NG];
+#pragma unroll
+    for (int i = 0; i < MG; ++i)
+#pragma unroll
+        for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t *wcr[NG], *wsr[NG];
+    bool wv[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        const int64_t n = n0 + j * 16 + (lane & 15);
+        wv[j] = n < N;
+        wcr[j] = wc + (wv[j] ? n : 0) * cb;
+        wsr[j] = ws + (wv[j] ? n : 0) * sb;
+    }
+    const uint8_t *xcr[MG], *xsr[MG];
+    bool xv[MG];
+#pragma unroll
+    for (int i = 0; i < MG; ++i) {
+        const int64_t m = i * 16 + (lane & 15);
+        xv[i] = m < M;
+        xcr[i] = ac + (xv[i] ? m : 0) * cb;
+        xsr[i] = as + (xv[i] ? m : 0) * sb;
+    }
+
+    for (int64_t c0 = wave; c0 < KC; c0 += (int64_t)WAVES * U) {
+        uint4 wq[U][NG], xq[U][MG];
+        uint32_t wsc[U][NG], xsc[U][MG];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = (c0 + (int64_t)u * WAVES) * 128 + kg;
+            const bool kin = k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                wq[u][j] = (kin && wv[j]) ? load_nt16(wcr[j] + (k >> 1)) : make_uint4(0, 0, 0, 0);
+                wsc[u][j] = (kin && wv[j]) ? *reinterpret_cast<const uint16_t *>(wsr[j] + (k >> 4)) : 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < MG; ++i) {
+                xq[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint4 *>(xcr[i] + (k >> 1)) : make_uint4(0, 0, 0, 0);
+                xsc[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint16_t *>(xsr[i] + (k >> 4)) : 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                half8_t b[NG];
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    const uint4 q = wq[u][j];
+                    const uint32_t w = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
+                    b[j] = expand8(w, e4m3_to_f16x2_over256(t < 2 ? (wsc[u][j] & 0xFFu) : (wsc[u][j] >> 8)));
+                }
+#pragma unroll
+                for (int i = 0; i < MG; ++i) {
+                    const uint4 q = xq[u][i];
+                    const uint32_t xw = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
+                    const half8_t a =
+                        expand8(xw, e4m3_to_f16x2_over256(t < 2 ? (xsc[u][i] & 0xFFu) : (xsc[u][i] >> 8)));
+#pragma unroll
+                    for (int j = 0; j < NG; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+                }
+            }
+    }
+
+    tile_reduce<MG, NG, WAVES, kOutBf16>(acc, *a_alpha, *w_alpha, M, N, n0, out, ld_out);
+}
+
+template <int MG, int NG, int WAVES, int U>
+hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, const float *aa, const uint8_t *wc,
+                            const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out,
+                            int out_type, int64_t ld_out, hipStream_t s) {
+    const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
+    if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (out_type == OUT_BF16)
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, true>), dim3((unsigned)nb), dim3(WAVES * 64), 0, s,
+                           ac, as, aa, wc, ws, wa, M, N, K, out, ld_out);
+    else
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, false>), dim3((unsigned)nb), dim3(WAVES * 64), 0, s,
+                           ac, as, aa, wc, ws, wa, M, N, K, out, ld_out);
+    return hipGetLastError();
+}
+
 __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
         for (int64_t c = threadIdx.x; c < row_bytes; c += blockDim.x) out[r * ld_bytes + c] = 0;
@@ -129,7 +247,7 @@ int skinny_cfg() {
     static int v = -1;
     if (v < 0) {
         const char *e = getenv("NVFP4_SKINNY_CFG");
-        v = !e ? 0 : !strcmp(e, "8x4") ? 1 : !strcmp(e, "16x4") ? 2 : !strcmp(e, "16x8") ? 3 : !strcmp(e, "8x8") ? 4 : 0;
+        v = !e ? 0 : !strcmp(e, "8x4") ? 1 : !strcmp(e, "16x4") ? 2 : !strcmp(e, "8x8") ? 4 : 0;
     }
     return v;
 }
@@ -139,17 +257,67 @@ hipError_t launch_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N,
                      int64_t ld_out, hipStream_t s) {
     switch (skinny_cfg()) {
         case 1: return launch_cfg<MG, NG, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
-        case 3: return launch_cfg<MG, NG, 16, 8>(a, w, M, N, K, out, out_type, ld_out, s);
         case 4: return launch_cfg<MG, NG, 8, 8>(a, w, M, N, K, out, out_type, ld_out, s);
         default: return launch_cfg<MG, NG, 16, 4>(a, w, M, N, K, out, out_type, ld_out, s);
     }
 }
 
+// NVFP4_DECODE_NG=1|2|4 forces the number of 16-column groups per
+// workgroup (tuning knob); by default it follows the layer width below.
+int decode_ng_knob() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("NVFP4_DECODE_NG");
+        v = e ? atoi(e) : 0;
+        if (v != 1 && v != 2 && v != 4) v = 0;
+    }
+    return v;
+}
+
+// With several 16-row groups of X, each X fragment a wave loads is reused
+// across NG weight-row groups; wide layers (N >= 6144 here: >= 192 workgroups
+// of 32 columns) take NG = 2 and 8 waves, very wide ones (N >= 16384) NG = 4,
+// narrow ones keep one group so every CU still gets a workgroup.
+template <int MG>
+hipError_t launch_mg_ng(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
+                        int out_type, int64_t ld_out, hipStream_t s) {
+    int ng = decode_ng_knob();
+    if (ng == 0) ng = MG == 1 ? 1 : N >= 16384 ? 4 : N >= 6144 ? 2 : 1;
+    if (ng == 4) return launch_cfg<MG, 4, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (ng == 2) return launch_cfg<MG, 2, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
+    return launch_mg<MG, 1>(a, w, M, N, K, out, out_type, ld_out, s);
+}
+
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
                               int out_type, int64_t ld_out, hipStream_t s) {
-    if (M <= 16) return launch_mg<1, 1>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (M <= 32) return launch_mg<2, 1>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (M <= 64) return launch_mg<4, 1>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (M <= 16) return launch_mg_ng<1>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (M <= 32) return launch_mg_ng<2>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (M <= 64) return launch_mg_ng<4>(a, w, M, N, K, out, out_type, ld_out, s);
+    return hipErrorInvalidValue;
+}
+
+template <int MG>
+hipError_t launch_nv_ng(const uint8_t *ac, const uint8_t *as, const float *aa, const uint8_t *wc, const uint8_t *ws,
+                        const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                        hipStream_t s) {
+    int ng = decode_ng_knob();
+    if (ng == 0) ng = MG == 4 && N >= 6144 ? 2 : 1;
+    switch (ng) {
+        case 2: return launch_nvfp4_cfg<MG, 2, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
+        case 4: return launch_nvfp4_cfg<MG, 4, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
+        default: return launch_nvfp4_cfg<MG, 1, 16, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
+    }
+}
+
+hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                               const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
+                               int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, hipStream_t s) {
+    if (M <= 16)
+        return launch_nv_ng<1>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
+    if (M <= 32)
+        return launch_nv_ng<2>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
+    if (M <= 64)
+        return launch_nv_ng<4>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
     return hipErrorInvalidValue;
 }
 

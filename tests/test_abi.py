@@ -79,6 +79,9 @@ def test_gemm_argument_errors(L):
     assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL  # null alpha
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL
     assert g(None, None, None, None, None, None, 0, 8, 32, None, 0, 8, None) == NVFP4_OK
+    odd = ctypes.c_void_p(0x1002)
+    assert g(FAKE, odd, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL  # scale align
+    assert b"4-byte aligned" in L.nvfp4_last_error()
     b = L.bf16_gemm
     assert b(FAKE, FAKE, 8, 8, 12, FAKE, 0, 8, None) == NVFP4_EUNSUPPORTED  # K % 8
     assert b(None, FAKE, 8, 8, 16, FAKE, 0, 8, None) == NVFP4_EINVAL

@@ -1,0 +1,111 @@
+"""GPU parity of NVFP4 x NVFP4 at decode shapes (M <= 64), the uniform-NVFP4
+and FP4-decode variants of Mix-Quant's ablations: nvfp4_gemm routes these to
+the split-K decode kernel when K % 32 == 0, and to the tile kernel
+otherwise.  Outputs are compared with the oracle's exact
+product under the gate of tests/parity.py; the BF16 output must equal the
+nearest-even rounding of the same kernel's FP32 output."""
+import numpy as np
+import pytest
+
+from nvfp4_prefill_gemm_amd import workloads as wl
+from tests import parity
+from tests.gpu_util import bf16_dev, bf16_out_to_f64, f32_dev, host, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from nvfp4_prefill_gemm_amd import binding
+
+    binding.lib()
+    return binding
+
+
+def _bf16_rne(y32):
+    return wl.bf16_bits_to_f32(wl.to_bf16_bits(y32.astype(np.float32))).astype(np.float64)
+
+
+def _run(nv, A, W, out_dtype):
+    import torch
+
+    def dev(q):
+        return u8_dev(q[0]), u8_dev(q[1]), f32_dev([q[2]])
+
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    y = nv.nvfp4_gemm(*dev(A), *dev(W), out_dtype=dt)
+    return host(y).astype(np.float64) if out_dtype == "f32" else bf16_out_to_f64(y)
+
+
+def _check(nv, A, W, ref, what):
+    y32 = _run(nv, A, W, "f32")
+    y16 = _run(nv, A, W, "bf16")
+    parity.assert_gemm_close(y32, ref, parity.GEMM_TOL_F32, what + " f32")
+    parity.assert_gemm_close(y16, ref, parity.GEMM_TOL_BF16, what + " bf16")
+    assert np.array_equal(y16, _bf16_rne(y32)), what + ": BF16 output is not the rounded FP32 output"
+    return y32
+
+
+@pytest.mark.parametrize("M", wl.PHASE_SPLIT_DECODE_M)
+def test_decode_nvfp4_qwen3_8b_full(nv, oracle_mod, M):
+    """Batch 1/8/64 through all four Qwen3-8B projections: activation
+    quantizer (dynamic alpha over the batch) bit-exact, full outputs."""
+    for layer, (name, K, N) in enumerate(wl.QWEN3_8B_LINEARS):
+        a = wl.activations(M, K, wl.rng(wl.PHASE_SPLIT_CONFIG_ID, layer, 0))
+        wt = wl.weights(N, K, wl.rng(wl.PHASE_SPLIT_CONFIG_ID, layer, 1))
+        A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+        say("decode nvfp4", name, M, N, K)
+        ac, asc, aal = nv.nvfp4_quantize(bf16_dev(a))
+        assert np.array_equal(host(ac), A[0]) and np.array_equal(host(asc), A[1]) and host(aal)[0] == A[2]
+        _check(nv, A, W, oracle_mod.gemm_exact(*A, *W), f"decode nvfp4 {name} M={M}")
+
+
+def _random_operand(g, rows, K, lo=0, hi=127):
+    codes = g.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    scales = g.integers(lo, hi, size=(rows, K // 16)).astype(np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 15, 96), (16, 17, 160), (17, 300, 4128), (33, 64, 288),
+                                   (64, 1000, 1056), (63, 31, 12288)])
+def test_decode_nvfp4_ragged(nv, oracle_mod, M, N, K):
+    """Ragged M/N/K (K not a multiple of the 128-wide chunk, N not a multiple
+    of 16, M in every row-group count), random codes and scale codes
+    including the E4M3 subnormals and 448."""
+    g = np.random.default_rng(M * 131 + N * 7 + K)
+    qa, sa = _random_operand(g, M, K)
+    qw, sw = _random_operand(g, N, K)
+    sa[:, 0] = np.arange(M, dtype=np.uint8) % 8  # zero and subnormal scales
+    sw[::3, -1] = 0x7E
+    A, W = (qa, sa, np.float32(3.1e-3)), (qw, sw, np.float32(7.6e-3))
+    say("decode nvfp4 ragged", M, N, K)
+    _check(nv, A, W, oracle_mod.gemm_exact(*A, *W), f"decode ragged {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 48), (8, 64, 80), (64, 40, 4112)])
+def test_decode_nvfp4_k_not_multiple_of_32(nv, oracle_mod, M, N, K):
+    """K % 32 != 0 takes the tile kernel; results still match the oracle."""
+    g = np.random.default_rng(K + N)
+    A = (*_random_operand(g, M, K, 100, 127), np.float32(1.0))
+    W = (*_random_operand(g, N, K, 100, 127), np.float32(0.5))
+    say("decode nvfp4 K%32 != 0", M, N, K)
+    _check(nv, A, W, oracle_mod.gemm_exact(*A, *W), f"decode K%32 {M}x{N}x{K}")
+
+
+def test_decode_kernel_agrees_with_tile_kernel(nv, oracle_mod):
+    """The same 8 activation rows through the decode kernel (M = 8) and, as
+    the first rows of a 65-row problem, through the tile kernel: both within
+    the gate of the exact product, and within twice the gate of each other."""
+    g = np.random.default_rng(5)
+    N, K = 520, 4096
+    A65 = (*_random_operand(g, 65, K, 110, 127), np.float32(0.01))
+    W = (*_random_operand(g, N, K, 110, 127), np.float32(0.02))
+    A8 = (A65[0][:8].copy(), A65[1][:8].copy(), A65[2])
+    ref65 = oracle_mod.gemm_exact(*A65, *W)
+    say("decode nvfp4 vs tile kernel", N, K)
+    y_dec = _check(nv, A8, W, ref65[:8], "decode kernel M=8")
+    y_tile = _check(nv, A65, W, ref65, "tile kernel M=65")[:8]
+    assert parity.floored_rel_err(y_dec, y_tile) <= 2 * parity.GEMM_TOL_F32
