@@ -358,17 +358,25 @@ def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
                torch.empty(max(nv.quantize_workspace_size(Md, L["K"]), 4), dtype=torch.uint8, device=dev))
               for L in layers]
 
+        # single-token decode: one kernel per layer, the activation quantized
+        # inside the decode GEMM (nvfp4_quant_gemm); larger batches quantize once
+        fused = [Md == 1 for L in layers]
+
         def dec4_step(c):
             for i, L in enumerate(layers):
                 ac, asc, aal, wsb = qa[i]
-                nv.nvfp4_quantize(xs[i], ac, asc, aal, workspace=wsb)
-                nv.nvfp4_gemm(ac, asc, aal, *wq[c][i], out=ys[i])
+                if fused[i]:
+                    nv.nvfp4_quant_gemm(xs[i], *wq[c][i], a_alpha=aal, out=ys[i], workspace=wsb)
+                else:
+                    nv.nvfp4_quantize(xs[i], ac, asc, aal, workspace=wsb)
+                    nv.nvfp4_gemm(ac, asc, aal, *wq[c][i], out=ys[i])
         us = graph_us(dec4_step, 4, 20)
         nbytes = sum(L["N"] * L["K"] * 9 // 16 + 2 * Md * L["K"] + Md * L["K"] * 9 // 16 + 2 * Md * L["N"]
                      for L in layers)
         dec4[str(Md)] = {"us_per_step": round(us, 1), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                          "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3),
-                         "speedup_vs_bf16_decode": round(decode[str(Md)]["us_per_step"] / us, 3)}
+                         "speedup_vs_bf16_decode": round(decode[str(Md)]["us_per_step"] / us, 3),
+                         "fused_layers": [L["name"] for L, f in zip(layers, fused) if f]}
     out["decode_nvfp4"] = dec4
     del wq
     return out

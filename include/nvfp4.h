@@ -105,10 +105,14 @@ size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t K);
 /*
  * Fused prefill linear: BF16 activations are quantized to NVFP4 inside the
  * GEMM's operand staging (Mix-Quant Section 3.3: quantization, dequantization
- * and the matrix product fused by the backend).  The result equals
- * nvfp4_quantize followed by nvfp4_gemm bit for bit whenever nvfp4_gemm takes
- * its tile kernel (M > 64 or K % 32 != 0; at decode shapes it sums in another
- * order); no codes or scales are written.
+ * and the matrix product fused by the backend).  No codes or scales are
+ * written.  For M <= 16 with M * K <= 196608 and K % 32 == 0 a decode kernel
+ * quantizes the batch into LDS (every workgroup forms the dynamic alpha
+ * itself); otherwise an amax pass precedes a tile kernel that quantizes in its
+ * operand staging.  The result equals nvfp4_quantize followed by nvfp4_gemm
+ * bit for bit whenever both run decode kernels (the condition above) or both
+ * run tile kernels (M > 64 or K % 32 != 0); in between they sum in different
+ * orders (both within FP32 rounding of the exact product).
  *   x_bf16 [M, ld_x] BF16 (16-byte aligned, ld_x % 8 == 0), K % 16 == 0
  *   a_alpha float[1]: written (dynamic) or read (static) as in nvfp4_quantize
  *   weights, out, out_dtype, ld_out as in nvfp4_gemm

@@ -141,6 +141,14 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
         const size_t need = (size_t)nparts * sizeof(uint32_t);
         if (!workspace || workspace_bytes < need)
             return fail(NVFP4_EWORKSPACE, "%s: dynamic alpha needs %zu workspace bytes", fn, need);
+    }
+    if (M <= nvfp4::kFusedDecodeMaxM && M * K <= nvfp4::kFusedDecodeMaxElems && K % 32 == 0)
+        return hip_status(nvfp4::launch_skinny_fused((const uint16_t *)x_bf16, ld_x, a_alpha,
+                                                     alpha_mode == NVFP4_ALPHA_DYNAMIC, w_codes, w_scales, w_alpha, M,
+                                                     N, K, out, out_dtype, ld_out, s),
+                          "fused decode kernel");
+    if (alpha_mode == NVFP4_ALPHA_DYNAMIC) {
+        const int nparts = nvfp4::amax_parts(M, K);
         if ((rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, M, K, ld_x, (uint32_t *)workspace,
                                                          nparts, s),
                              "amax kernel")))

@@ -46,6 +46,20 @@ hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, 
                                int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
                                hipStream_t s);
 
+// Fused decode (BF16 activations quantized into LDS by every workgroup):
+// M <= 16, M * K <= kFusedDecodeMaxElems, K % 32 == 0, x rows 16-byte
+// aligned; dynamic != 0 computes alpha_A in every workgroup.
+hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, int dynamic,
+                               const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                               int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                               hipStream_t s);
+
+// nvfp4_quant_gemm routes M <= kFusedDecodeMaxM with M * K <=
+// kFusedDecodeMaxElems (108 KB of codes and scales in LDS: every Qwen3-8B
+// layer at 16 tokens) to the fused decode kernel.
+constexpr int64_t kFusedDecodeMaxM = 16;
+constexpr int64_t kFusedDecodeMaxElems = 16 * 12288;
+
 // Largest M routed to the skinny decode kernels by bf16_gemm and nvfp4_gemm.
 constexpr int64_t kSkinnyMaxM = 64;
 

@@ -18,6 +18,15 @@
 // for A and W, which leaves the dot product unchanged).  Codes are expanded
 // exactly to q * sigma in FP16 in registers; alpha_A * alpha_W is applied in
 // the epilogue as in the prefill GEMM.
+//
+// Fused decode (nvfp4_quant_gemm with M * K <= 196608): the workgroup first
+// quantizes the BF16 batch itself, one 8-element group per thread with the
+// quantizer's own Eq. 3 / Eq. 2 functions, into LDS (a dynamic tensor scale
+// is formed from a first pass over the batch; every workgroup derives the
+// same alpha_A and workgroup 0 stores it), then runs the loop above with the
+// activation codes read from LDS.  Codes, scales and the summation order
+// equal those of quantize followed by the decode GEMM, so the two paths agree
+// bit for bit.
 #include <stdlib.h>
 #include <string.h>
 
@@ -137,13 +146,19 @@ hipError_t launch_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N
     return hipGetLastError();
 }
 
+// Source of the A operand of the decode kernel.
+enum ASrc { A_NVFP4 = 0, A_BF16_DYNAMIC = 1, A_BF16_STATIC = 2 };
+
 // NVFP4 x NVFP4, M <= MG*16, NG*16 weight rows per workgroup, K % 32 == 0,
-// 16-byte aligned codes and 4-byte aligned scales.
-template <int MG, int NG, int WAVES, int U, bool kOutBf16>
+// 16-byte aligned codes and 4-byte aligned scales.  kA != A_NVFP4: A is
+// BF16 [M, ld_x] (16-byte aligned rows, MG == 1), quantized into LDS
+// (M * K * 9 / 16 bytes of dynamic shared memory).
+template <int MG, int NG, int WAVES, int U, bool kOutBf16, int kA = A_NVFP4>
 __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
-    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ a_alpha,
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, float *__restrict__ a_alpha,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, const float *__restrict__ w_alpha, int64_t M,
-    int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out) {
+    int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out, const uint16_t *__restrict__ x, int64_t ld_x) {
+    static_assert(kA == A_NVFP4 || MG == 1, "BF16 activations: one 16-row group");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int64_t cb = K >> 1, sb = K >> 4;  // code and scale bytes per row
@@ -174,6 +189,62 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         xcr[i] = ac + (xv[i] ? m : 0) * cb;
         xsr[i] = as + (xv[i] ? m : 0) * sb;
     }
+    float alpha_a = 0.0f;
+    if constexpr (kA != A_NVFP4) {
+        // quantize the whole batch into LDS: codes [M][K/2], then scales [M][K/16]
+        extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+        uint8_t *lc = xlds, *ls = xlds + M * cb;
+        // 32-bit indexing: M * K <= kFusedDecodeMaxElems
+        const uint32_t octs = (uint32_t)(K >> 3), total = (uint32_t)M * octs;  // total is even (K % 32 == 0)
+        auto load_oct = [&](uint32_t o) __attribute__((always_inline)) {
+            if (o >= total) return make_uint4(0, 0, 0, 0);
+            const uint32_t r = o / octs;
+            return *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld_x + (o - r * octs) * 8);
+        };
+        if constexpr (kA == A_BF16_STATIC) {
+            alpha_a = *a_alpha;
+        } else {
+            uint32_t am = 0;
+            for (uint32_t o = threadIdx.x; o < total; o += WAVES * 64) {
+                const uint4 v = load_oct(o);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
+            }
+            for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
+            __shared__ uint32_t wmax[WAVES];
+            if (lane == 0) wmax[wave] = am;
+            __syncthreads();
+            uint32_t t = wmax[0];
+#pragma unroll
+            for (int v = 1; v < WAVES; ++v) t = max(t, wmax[v]);
+            alpha_a = div_rn(bf16_bits_to_f32(t), kAlphaDen);
+            if (blockIdx.x == 0 && threadIdx.x == 0) *a_alpha = alpha_a;
+        }
+        // thread pairs (t, t ^ 1) hold the two halves of a 16-element block
+        for (uint32_t base = 0; base < total; base += WAVES * 64) {
+            const uint32_t o = base + threadIdx.x;
+            const uint4 v = load_oct(o);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            uint32_t am = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
+            const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha_a);
+            if (o < total) {
+                const uint32_t r = o / octs, oc = o - r * octs;
+                *reinterpret_cast<uint32_t *>(lc + r * cb + oc * 4) = quant8(w4, bs.d);
+                if ((oc & 1) == 0) ls[r * sb + (oc >> 1)] = (uint8_t)bs.code;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MG; ++i) {
+            const int64_t m = i * 16 + (lane & 15);
+            xcr[i] = lc + (xv[i] ? m : 0) * cb;
+            xsr[i] = ls + (xv[i] ? m : 0) * sb;
+        }
+    }
 
     for (int64_t c0 = wave; c0 < KC; c0 += (int64_t)WAVES * U) {
         uint4 wq[U][NG], xq[U][MG];
@@ -188,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
                 wsc[u][j] = (kin && wv[j]) ? *reinterpret_cast<const uint16_t *>(wsr[j] + (k >> 4)) : 0u;
             }
 #pragma unroll
-            for (int i = 0; i < MG; ++i) {
+            for (int i = 0; i < MG; ++i) {  // global memory, or LDS for the fused path
                 xq[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint4 *>(xcr[i] + (k >> 1)) : make_uint4(0, 0, 0, 0);
                 xsc[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint16_t *>(xsr[i] + (k >> 4)) : 0u;
             }
@@ -217,21 +288,34 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             }
     }
 
-    tile_reduce<MG, NG, WAVES, kOutBf16>(acc, *a_alpha, *w_alpha, M, N, n0, out, ld_out);
+    tile_reduce<MG, NG, WAVES, kOutBf16>(acc, kA == A_NVFP4 ? *a_alpha : alpha_a, *w_alpha, M, N, n0, out, ld_out);
 }
 
-template <int MG, int NG, int WAVES, int U>
-hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, const float *aa, const uint8_t *wc,
-                            const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out,
-                            int out_type, int64_t ld_out, hipStream_t s) {
+template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4>
+hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
+                            const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                            hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0) {
     const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const size_t lds = kA == A_NVFP4 ? 0 : (size_t)(M * K / 2 + M * K / 16);
+    if (kA != A_NVFP4) {
+        static bool attr[2] = {false, false};
+        const int o = out_type == OUT_BF16;
+        if (!attr[o]) {
+            const void *f = o ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>
+                              : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, false, kA>;
+            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(kFusedDecodeMaxElems * 9 / 16));
+            if (e != hipSuccess) return e;
+            attr[o] = true;
+        }
+    }
     if (out_type == OUT_BF16)
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, true>), dim3((unsigned)nb), dim3(WAVES * 64), 0, s,
-                           ac, as, aa, wc, ws, wa, M, N, K, out, ld_out);
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>), dim3((unsigned)nb), dim3(WAVES * 64),
+                           lds, s, ac, as, aa, wc, ws, wa, M, N, K, out, ld_out, x, ld_x);
     else
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, false>), dim3((unsigned)nb), dim3(WAVES * 64), 0, s,
-                           ac, as, aa, wc, ws, wa, M, N, K, out, ld_out);
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, false, kA>), dim3((unsigned)nb), dim3(WAVES * 64),
+                           lds, s, ac, as, aa, wc, ws, wa, M, N, K, out, ld_out, x, ld_x);
     return hipGetLastError();
 }
 
@@ -297,9 +381,10 @@ hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, i
 }
 
 template <int MG>
-hipError_t launch_nv_ng(const uint8_t *ac, const uint8_t *as, const float *aa, const uint8_t *wc, const uint8_t *ws,
-                        const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                        hipStream_t s) {
+hipError_t launch_nv_ng(const uint8_t *ac, const uint8_t *as, const float *aa_in, const uint8_t *wc,
+                        const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type,
+                        int64_t ld_out, hipStream_t s) {
+    float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
     int ng = decode_ng_knob();
     if (ng == 0) ng = MG == 4 && N >= 6144 ? 2 : 1;
     switch (ng) {
@@ -319,6 +404,17 @@ hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, 
     if (M <= 64)
         return launch_nv_ng<4>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, int dynamic, const uint8_t *w_codes,
+                               const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K,
+                               void *out, int out_type, int64_t ld_out, hipStream_t s) {
+    if (M > 16 || M * K > kFusedDecodeMaxElems) return hipErrorInvalidValue;
+    if (dynamic)
+        return launch_nvfp4_cfg<1, 1, 16, 2, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M,
+                                                             N, K, out, out_type, ld_out, s, x, ld_x);
+    return launch_nvfp4_cfg<1, 1, 16, 2, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
+                                                        K, out, out_type, ld_out, s, x, ld_x);
 }
 
 hipError_t launch_fill_zero(void *out, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s) {

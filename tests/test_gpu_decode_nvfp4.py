@@ -109,3 +109,75 @@ def test_decode_kernel_agrees_with_tile_kernel(nv, oracle_mod):
     y_dec = _check(nv, A8, W, ref65[:8], "decode kernel M=8")
     y_tile = _check(nv, A65, W, ref65, "tile kernel M=65")[:8]
     assert parity.floored_rel_err(y_dec, y_tile) <= 2 * parity.GEMM_TOL_F32
+
+
+@pytest.mark.parametrize("M,N,K,ld_pad", [(1, 6144, 4096, 0), (1, 4096, 12288, 0), (2, 300, 4128, 8),
+                                          (8, 24576, 4096, 0), (13, 17, 96, 24), (16, 1000, 1056, 0),
+                                          (16, 64, 12288, 0), (1, 520, 65536, 0)])
+def test_fused_decode_equals_quantize_then_gemm(nv, oracle_mod, M, N, K, ld_pad):
+    """nvfp4_quant_gemm with M <= 16 and M * K <= 196608 quantizes the batch
+    inside the decode kernel: alpha, and the output in FP32 and BF16, equal
+    nvfp4_quantize followed by nvfp4_gemm bit for bit (dynamic and static
+    alpha, strided x, the size limit itself); both within the gate of the
+    oracle's exact product."""
+    import torch
+
+    g = np.random.default_rng(M * 17 + N + K)
+    a = wl.activations(M, K, g)
+    wt = wl.weights(N, K, g)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    ref = oracle_mod.gemm_exact(*A, *W)
+    wc, wsc, wal = u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]])
+    xfull = torch.zeros((M, K + ld_pad), dtype=torch.bfloat16, device="cuda")
+    xfull[:, :K] = bf16_dev(a)
+    x = xfull[:, :K]
+    say("fused decode vs quantize+gemm", M, N, K, ld_pad)
+    for od in (torch.float32, torch.bfloat16):
+        ac, asc, aal = nv.nvfp4_quantize(x)
+        y_unf = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=od)
+        y_fus, alpha = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=od)
+        assert host(alpha)[0] == host(aal)[0] == A[2]
+        assert torch.equal(y_fus, y_unf), f"fused decode differs from quantize + gemm ({od})"
+        y_st, _ = nv.nvfp4_quant_gemm(x, wc, wsc, wal, a_alpha=f32_dev([A[2]]), static_alpha=True, out_dtype=od)
+        assert torch.equal(y_st, y_fus)
+        tol = parity.GEMM_TOL_F32 if od == torch.float32 else parity.GEMM_TOL_BF16
+        parity.assert_gemm_close(y_fus.float().cpu().numpy(), ref, tol, f"fused decode {M}x{N}x{K}")
+
+
+def test_fused_decode_zero_batch_and_zero_rows(nv, oracle_mod):
+    """An all-zero batch gives alpha 0 and a zero output; a batch whose rows
+    are partly zero matches the oracle."""
+    import torch
+
+    K, N = 256, 64
+    wt = wl.weights(N, K, np.random.default_rng(1))
+    W = oracle_mod.quantize(wt)
+    wc, wsc, wal = u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]])
+    say("fused decode zero batch")
+    y, alpha = nv.nvfp4_quant_gemm(torch.zeros((3, K), dtype=torch.bfloat16, device="cuda"), wc, wsc, wal,
+                                   out_dtype=torch.float32)
+    assert host(alpha)[0] == 0.0 and not host(y).any()
+    a = wl.activations(5, K, np.random.default_rng(2))
+    a[1] = 0
+    a[3] = 0x8000  # -0.0
+    A = oracle_mod.quantize(a)
+    y, alpha = nv.nvfp4_quant_gemm(bf16_dev(a), wc, wsc, wal, out_dtype=torch.float32)
+    assert host(alpha)[0] == A[2]
+    parity.assert_gemm_close(host(y), oracle_mod.gemm_exact(*A, *W), parity.GEMM_TOL_F32, "partly zero batch")
+
+
+def test_fused_past_decode_limit_within_gate(nv, oracle_mod):
+    """M <= 16 with M * K > 196608 takes the tile fused kernel; it agrees with
+    the oracle (the unfused decode kernel sums in another order)."""
+    import torch
+
+    M, N, K = 16, 96, 12320
+    g = np.random.default_rng(77)
+    a = wl.activations(M, K, g)
+    wt = wl.weights(N, K, g)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    say("fused past decode limit", M, N, K)
+    y, alpha = nv.nvfp4_quant_gemm(bf16_dev(a), u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]]),
+                                   out_dtype=torch.float32)
+    assert host(alpha)[0] == A[2]
+    parity.assert_gemm_close(host(y), oracle_mod.gemm_exact(*A, *W), parity.GEMM_TOL_F32, "fused tile M=16")
