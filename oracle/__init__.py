@@ -65,6 +65,7 @@ def _load():
         "oracle_amax_bf16": (F, [P, I64, I64, I64]),
         "oracle_tensor_alpha": (F, [F]),
         "oracle_quantize": (I, [P, I64, I64, I64, I, P, P, P, I]),
+        "oracle_quantize_f32": (I, [P, I64, I64, I64, I, P, P, P, I]),
         "oracle_dequantize": (None, [P, P, F, I64, I64, P]),
         "oracle_gemm_exact": (I, [P, P, F, P, P, F, I64, I64, I64, P, I]),
         "oracle_gemm_exact_pairs": (I, [P, P, F, P, P, F, I64, I64, I64, P, P, I64, P, I]),
@@ -159,6 +160,21 @@ def quantize(x_bits: np.ndarray, alpha: float | None = None, nthreads: int = 0):
                                  _ptr(codes), _ptr(scales), nthreads)
     if rc != 0:
         raise ValueError("oracle_quantize: cols must be a multiple of 16")
+    return codes, scales, np.float32(a[0])
+
+
+def quantize_f32(x: np.ndarray, alpha: float | None = None, nthreads: int = 0):
+    """Quantize an FP32 matrix [rows, cols] (each value as it is, e.g. a GEMM
+    output); alpha as in quantize().  Returns (codes, scales, alpha)."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    scales = np.empty((rows, cols // 16), dtype=np.uint8)
+    a = np.array([0.0 if alpha is None else alpha], dtype=np.float32)
+    rc = _load().oracle_quantize_f32(_ptr(x), rows, cols, cols, 0 if alpha is None else 1, _ptr(a),
+                                     _ptr(codes), _ptr(scales), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_quantize_f32: cols must be a multiple of 16")
     return codes, scales, np.float32(a[0])
 
 

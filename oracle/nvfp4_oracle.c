@@ -173,8 +173,34 @@ float oracle_amax_bf16(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld
 /* Tensor-level scale: alpha = amax / (q_max * E4M3 max) = amax / (6 * 448). */
 float oracle_tensor_alpha(float amax) { return amax / (6.0f * 448.0f); }
 
+/* One 16-element block v (FP32 values) with tensor scale alpha: Eq. (3) for
+ * its E4M3 scale code, Eq. (2) for its 16 E2M1 codes, packed two per byte
+ * (element 2j in the low nibble) into codes8[0..7].                         */
+static void quant_block(const float v[16], float alpha, uint8_t *scale, uint8_t codes8[8]) {
+    float amax_b = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax_b) amax_b = a;
+    }
+    /* Eq. (3): sigma = Pi_E4M3( amax_b / (alpha * q_max) ) */
+    float t = alpha * 6.0f;
+    float s = (t > 0.0f) ? amax_b / t : 0.0f;
+    int sc = oracle_e4m3_encode(s);
+    float sigma = (float)oracle_e4m3_value(sc);
+    *scale = (uint8_t)sc;
+    /* Eq. (2): q_i = Pi_FP4( x_i / (alpha * sigma) ) */
+    float d = alpha * sigma;
+    uint8_t codes[16];
+    for (int i = 0; i < 16; ++i) {
+        float y = (d > 0.0f) ? v[i] / d : copysignf(0.0f, v[i]);
+        codes[i] = (uint8_t)oracle_e2m1_encode(y);
+    }
+    for (int j = 0; j < 8; ++j) codes8[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+}
+
 typedef struct {
-    const uint16_t *x;
+    const uint16_t *x;   /* BF16 input, or NULL */
+    const float *xf;     /* FP32 input, or NULL */
     int64_t cols, ld;
     float alpha;
     uint8_t *codes, *scales;
@@ -184,30 +210,11 @@ static void quant_rows(void *p, int64_t r0, int64_t r1) {
     quant_ctx *q = (quant_ctx *)p;
     const int64_t nb = q->cols / 16;
     for (int64_t r = r0; r < r1; ++r) {
-        const uint16_t *xr = q->x + r * q->ld;
         for (int64_t b = 0; b < nb; ++b) {
             float v[16];
-            float amax_b = 0.0f;
-            for (int i = 0; i < 16; ++i) {
-                v[i] = bf16_to_float(xr[b * 16 + i]);
-                float a = fabsf(v[i]);
-                if (a > amax_b) amax_b = a;
-            }
-            /* Eq. (3): sigma = Pi_E4M3( amax_b / (alpha * q_max) ) */
-            float t = q->alpha * 6.0f;
-            float s = (t > 0.0f) ? amax_b / t : 0.0f;
-            int sc = oracle_e4m3_encode(s);
-            float sigma = (float)oracle_e4m3_value(sc);
-            q->scales[r * nb + b] = (uint8_t)sc;
-            /* Eq. (2): q_i = Pi_FP4( x_i / (alpha * sigma) ) */
-            float d = q->alpha * sigma;
-            uint8_t codes[16];
-            for (int i = 0; i < 16; ++i) {
-                float y = (d > 0.0f) ? v[i] / d : copysignf(0.0f, v[i]);
-                codes[i] = (uint8_t)oracle_e2m1_encode(y);
-            }
-            for (int j = 0; j < 8; ++j)
-                q->codes[r * (q->cols / 2) + b * 8 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+            for (int i = 0; i < 16; ++i)
+                v[i] = q->x ? bf16_to_float(q->x[r * q->ld + b * 16 + i]) : q->xf[r * q->ld + b * 16 + i];
+            quant_block(v, q->alpha, &q->scales[r * nb + b], &q->codes[r * (q->cols / 2) + b * 8]);
         }
     }
 }
@@ -221,7 +228,29 @@ int oracle_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, i
     if (cols % 16 != 0 || ld < cols || rows < 0) return -1;
     tables();
     if (alpha_mode == 0) *alpha = oracle_tensor_alpha(oracle_amax_bf16(x, rows, cols, ld));
-    quant_ctx q = {x, cols, ld, *alpha, codes, scales};
+    quant_ctx q = {x, NULL, cols, ld, *alpha, codes, scales};
+    parallel_rows(quant_rows, &q, rows, nthreads);
+    return 0;
+}
+
+/* The same Eq. (3) / Eq. (2) steps on an FP32 tensor (a GEMM output that is
+ * quantized for the next linear layer), each value taken as it is (no
+ * rounding to BF16 first).  alpha_mode as in oracle_quantize; the dynamic
+ * amax is max |x| over the FP32 values.                                    */
+int oracle_quantize_f32(const float *x, int64_t rows, int64_t cols, int64_t ld, int alpha_mode, float *alpha,
+                        uint8_t *codes, uint8_t *scales, int nthreads) {
+    if (cols % 16 != 0 || ld < cols || rows < 0) return -1;
+    tables();
+    if (alpha_mode == 0) {
+        float m = 0.0f;
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t c = 0; c < cols; ++c) {
+                float a = fabsf(x[r * ld + c]);
+                if (a > m) m = a;
+            }
+        *alpha = oracle_tensor_alpha(m);
+    }
+    quant_ctx q = {NULL, x, cols, ld, *alpha, codes, scales};
     parallel_rows(quant_rows, &q, rows, nthreads);
     return 0;
 }
