@@ -268,6 +268,26 @@ def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
     fused_ms = s.elapsed_time(e) / reps
     out["fused_tflops"] = round(flops_step / (fused_ms * 1e-3) / 1e12, 2)
 
+    # NVFP4 GEMM whose epilogue quantizes Y to NVFP4 for the next layer
+    # (static output scale), same layers and activations
+    yq = [(torch.empty((M, L["N"] // 2), dtype=torch.uint8, device=dev),
+           torch.empty((M, L["N"] // 16), dtype=torch.uint8, device=dev)) for L in layers]
+    y_alpha = torch.tensor([0.02], dtype=torch.float32, device=dev)
+
+    def qo_step():
+        for L, (yc, ysc) in zip(layers, yq):
+            nv.nvfp4_gemm_quant_out(L["ac"], L["asc"], L["aal"], L["wc"], L["ws"], L["wa"], y_alpha, yc, ysc)
+    for _ in range(2):
+        qo_step()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        qo_step()
+    e.record()
+    torch.cuda.synchronize()
+    out["quant_out_gemm_tflops"] = round(flops_step / (s.elapsed_time(e) / reps * 1e-3) / 1e12, 2)
+    del yq
+
     # MXFP4 (E2M1 + E8M0 per 32) prefill of the same layers on the block-scaled
     # FP4 MFMA: activation quantizer + GEMM, weights quantized once
     mx = []

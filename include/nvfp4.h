@@ -99,6 +99,24 @@ int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_a
                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
                int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out, void *stream);
 
+/*
+ * NVFP4 x NVFP4 GEMM whose output is itself NVFP4, for the next linear layer
+ * (Mix-Quant Section 3.3: the backend fuses quantization into the matrix
+ * product).  Y = xhatA * xhatW^T is formed as nvfp4_gemm's FP32 output
+ * (y = (acc * alpha_A) * alpha_W) and quantized in the epilogue with Eq. 3
+ * and Eq. 2 against a static output tensor scale:
+ *   y_codes [M, N/2] uint8 out (4-byte aligned), y_scales [M, N/16] uint8 out,
+ *   y_alpha float[1] in (device): the output tensor scale, e.g. calibrated.
+ *   N % 16 == 0, K % 16 == 0; operands as in nvfp4_gemm.  The codes equal
+ *   those the quantizer gives for the FP32 output of the same product.
+ * A dynamic output scale would need the whole output's amax before any
+ * block is quantized, so it is not offered here.
+ */
+int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                         const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
+                         int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales, const float *y_alpha,
+                         void *stream);
+
 /* Bytes of device workspace nvfp4_quant_gemm needs (dynamic-alpha mode). */
 size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t K);
 

@@ -9,7 +9,8 @@ from . import workloads  # noqa: F401
 
 def __getattr__(name):
     # the binding imports torch; load it on first use of an entry point
-    if name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_quant_gemm", "bf16_gemm", "mxfp4_quantize", "mxfp4_gemm",
+    if name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_quant_gemm", "nvfp4_gemm_quant_out", "bf16_gemm",
+                "mxfp4_quantize", "mxfp4_gemm",
                 "binding", "lib", "last_error"):
         import importlib
 

@@ -28,6 +28,7 @@ _SIGNATURES = {
     "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
+    "nvfp4_gemm_quant_out": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quant_gemm": (_I, [_P, _I64, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "bf16_gemm": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
@@ -138,6 +139,28 @@ def nvfp4_gemm(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, out: torc
                           _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _stream(stream))
     _check("nvfp4_gemm", rc)
     return out
+
+
+def nvfp4_gemm_quant_out(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, y_alpha: torch.Tensor,
+                         y_codes: torch.Tensor | None = None, y_scales: torch.Tensor | None = None, stream=None):
+    """NVFP4 GEMM with an NVFP4 output (static output scale y_alpha, float32 [1]).
+    Returns (y_codes uint8 [M, N/2], y_scales uint8 [M, N/16])."""
+    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
+        _dev(t, n, torch.uint8)
+    _dev(y_alpha, "y_alpha", torch.float32)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("A and W disagree on K")
+    if y_codes is None:
+        y_codes = torch.empty((M, N // 2), dtype=torch.uint8, device=a_codes.device)
+    if y_scales is None:
+        y_scales = torch.empty((M, N // 16), dtype=torch.uint8, device=a_codes.device)
+    rc = lib().nvfp4_gemm_quant_out(_ptr(a_codes), _ptr(a_scales), _ptr(a_alpha), _ptr(w_codes), _ptr(w_scales),
+                                    _ptr(w_alpha), M, N, K, _ptr(y_codes), _ptr(y_scales), _ptr(y_alpha),
+                                    _stream(stream))
+    _check("nvfp4_gemm_quant_out", rc)
+    return y_codes, y_scales
 
 
 def quant_gemm_workspace_size(M: int, K: int) -> int:

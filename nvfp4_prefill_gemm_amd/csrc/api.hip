@@ -116,6 +116,30 @@ int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_a
                       "nvfp4 gemm kernel");
 }
 
+int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                         const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
+                         int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales, const float *y_alpha,
+                         void *stream) {
+    const char *fn = "nvfp4_gemm_quant_out";
+    if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (K % 16 != 0) return fail(NVFP4_EINVAL, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
+    if (N % 16 != 0) return fail(NVFP4_EINVAL, "%s: N (%lld) must be a multiple of 16", fn, (long long)N);
+    if (M == 0 || N == 0) return ok();
+    if (!y_codes || !y_scales || !y_alpha) return fail(NVFP4_EINVAL, "%s: null output pointer", fn);
+    if (!aligned(y_codes, 4)) return fail(NVFP4_EINVAL, "%s: y_codes must be 4-byte aligned", fn);
+    hipStream_t s = as_stream(stream);
+    int rc;
+    if (K == 0) {  // Y = 0: zero codes and zero scales
+        if ((rc = hip_status(nvfp4::launch_fill_zero(y_codes, M, N / 2, N / 2, 1, s), "fill kernel"))) return rc;
+        return hip_status(nvfp4::launch_fill_zero(y_scales, M, N / 16, N / 16, 1, s), "fill kernel");
+    }
+    if ((rc = check_nvfp4(a_codes, a_scales, a_alpha, "A", fn))) return rc;
+    if ((rc = check_nvfp4(w_codes, w_scales, w_alpha, "W", fn))) return rc;
+    return hip_status(nvfp4::launch_gemm_nvfp4_quant_out(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N,
+                                                         K, y_codes, y_scales, y_alpha, s),
+                      "nvfp4 gemm kernel (quantized output)");
+}
+
 size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t K) { return nvfp4_quantize_workspace_size(M, K); }
 
 int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha_mode, const uint8_t *w_codes,

@@ -29,6 +29,8 @@
 
 #include <type_traits>
 
+#include <utility>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 #include "tiling.hpp"
@@ -54,6 +56,17 @@ using SmallTile = TileCfg<128, 128, 2, 2, 2>; // 4 waves of 64 x 64
 // LDS tile layout: rows of 64 halves (eight 16-byte chunks), swizzled by lds_swz.
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ lds_swz(row)) << 3); }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled
+// by construction (array indices inside f are compile-time constants).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
 struct GemmArgs {
     const void *a;          // A codes or A BF16
     const uint8_t *a_scales;
@@ -64,6 +77,8 @@ struct GemmArgs {
     int64_t M, N, K, lda;   // lda: BF16 row stride (fused / BF16 A)
     void *out;
     int64_t ld_out;
+    uint8_t *out_scales;      // NVFP4 output: E4M3 block scales [M, N/16]
+    const float *out_alpha;   // NVFP4 output: static tensor scale
 };
 
 // ---------------------------------------------------------------- loaders
@@ -240,7 +255,7 @@ struct KindTraits<KIND_BF16> {
 // range and K % 64 == 0): no bounds checks, so each pipeline step is one
 // basic block the scheduler can interleave.  NVFP4 operands are prefetched
 // two K steps ahead in registers (18 VGPRs a stage); BF16 operands one step.
-template <class C, int kKind, bool kOutBf16, bool kGuard>
+template <class C, int kKind, int kOut, bool kGuard>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t n0,
                                           typename KindTraits<kKind>::lds_t *lds) {
     typedef typename KindTraits<kKind>::lds_t lds_t;
@@ -387,6 +402,100 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
         sa = *g.a_alpha;
         sw = *g.w_alpha;
     }
+    if constexpr (kOut == OUT_NVFP4) {
+        // Quantized output for the next layer (Eq. 3 / Eq. 2 with the static
+        // output scale).  Each wave stages its results through LDS one 32-row
+        // slab at a time, so that a lane then owns whole 16-element blocks of
+        // a row: block amax, block scale and the 16 codes are formed in-lane
+        // and stored as 8 bytes + 1 scale byte.  N % 16 == 0.
+        static_assert(C::WN % 64 == 0 && C::WM % 32 == 0, "quantizing epilogue: wave tiles of 64k columns");
+        constexpr int SLD = C::WN + 8;  // padded row stride (floats): the two half-waves hit different banks
+        constexpr int BPR = C::WN / 16, NBL = 32 * BPR / 64;  // blocks per slab row, blocks per lane
+        const float ya = *g.out_alpha;
+        const int64_t ldc = g.N >> 1, lds_ = g.N >> 4;
+        uint8_t *codes = reinterpret_cast<uint8_t *>(g.out);
+        const float t6 = ya * kQmax, rt6 = t6 > 0.0f ? div_rn(1.0f, t6) : 0.0f;
+        const bool tfast = (t6 >= 0x1p-100f) & (t6 <= 0x1p100f);
+        float *slab = reinterpret_cast<float *>(lds) + wave * (32 * SLD);
+        __syncthreads();  // every wave is done with the operand buffers
+        static_for<TM>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            // fragment layout -> row-major slab (32 rows x 128 columns)
+            static_for<TN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                static_for<16>([&](auto rc) __attribute__((always_inline)) {
+                    constexpr int r = decltype(rc)::value;
+                    const int rl = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    slab[rl * SLD + j * 32 + (lane & 31)] = (acc[i][j][r] * sa) * sw;
+                });
+            });
+            // 32 rows x BPR blocks: lane handles blocks lane + 64 q
+#pragma unroll
+            for (int q = 0; q < NBL; ++q) {
+                const int bi = lane + 64 * q, rl = bi / BPR, blk = bi % BPR;
+                float v[16];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float4 t = *reinterpret_cast<const float4 *>(slab + rl * SLD + blk * 16 + 4 * e);
+                    v[4 * e] = t.x;
+                    v[4 * e + 1] = t.y;
+                    v[4 * e + 2] = t.z;
+                    v[4 * e + 3] = t.w;
+                }
+                uint32_t am = 0;
+                bool tiny = false;  // a nonzero |v| below 2^-100 (outside the fast division's range)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t ab = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+                    am = max(am, ab);
+                    tiny = tiny | ((ab != 0u) & (ab < 0x0D800000u));  // 2^-100 = 0x0D800000
+                }
+                const float amax = __uint_as_float(am);
+                // Eq. 3 with the tensor-wide reciprocal (Markstein) when it qualifies
+                float sq;
+                if (__all(tfast & (amax <= t6 * 0x1p120f) & ((amax == 0.0f) | (amax >= 0x1p-100f)))) {
+                    const float q0 = amax * rt6;
+                    sq = __builtin_fmaf(__builtin_fmaf(-q0, t6, amax), rt6, q0);
+                } else {
+                    sq = t6 > 0.0f ? div_rn(amax, t6) : 0.0f;
+                }
+                const uint32_t code = e4m3_encode_sel(sq);
+                const float d = ya * e4m3_decode(code);
+                // Eq. 2: one reciprocal per block, Markstein per element
+                const float rd = d > 0.0f ? div_rn(1.0f, d) : 0.0f;
+                float qv[16];
+                if (__all((d >= 0x1p-100f) & (d <= 0x1p100f) & !tiny & (amax <= d * 0x1p120f))) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float q0 = v[e] * rd;
+                        qv[e] = __builtin_fmaf(__builtin_fmaf(-q0, d, v[e]), rd, q0);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        qv[e] = d > 0.0f ? div_rn(v[e], d) : __uint_as_float(__float_as_uint(v[e]) & 0x80000000u);
+                }
+                // nearest-even E2M1 with saturation, sign kept (hardware convert)
+                uint32_t w0 = 0, w1 = 0;
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[0], qv[1], 1.0f, 0);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[2], qv[3], 1.0f, 1);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[4], qv[5], 1.0f, 2);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[6], qv[7], 1.0f, 3);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[8], qv[9], 1.0f, 0);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[10], qv[11], 1.0f, 1);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[12], qv[13], 1.0f, 2);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[14], qv[15], 1.0f, 3);
+                const int64_t row = m0 + wm * C::WM + i * 32 + rl, col = n0 + wn * C::WN + blk * 16;
+                if ((!kGuard | (row < g.M)) & (!kGuard | (col < g.N))) {
+                    uint32_t *cp = reinterpret_cast<uint32_t *>(codes + row * ldc + (col >> 1));
+                    cp[0] = w0;
+                    cp[1] = w1;
+                    g.out_scales[row * lds_ + (col >> 4)] = (uint8_t)code;
+                }
+            }
+        });
+        return;
+    } else {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -399,15 +508,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
                 if (kGuard && row >= g.M) continue;
                 float y = acc[i][j][r];
                 if (kKind != KIND_BF16) y = (y * sa) * sw;
-                if (kOutBf16)
+                if (kOut == OUT_BF16)
                     reinterpret_cast<__bf16 *>(g.out)[row * g.ld_out + col] = (__bf16)y;
                 else
                     reinterpret_cast<float *>(g.out)[row * g.ld_out + col] = y;
             }
         }
+    }
 }
 
-template <class C, int kKind, bool kOutBf16>
+template <class C, int kKind, int kOut>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_kernel(GemmArgs g) {
     typedef typename KindTraits<kKind>::lds_t lds_t;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -417,18 +527,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_kernel(GemmArgs g) {
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const bool full = m0 + C::BM <= g.M && n0 + C::BN <= g.N && (g.K & (BK - 1)) == 0;
     if (full)
-        gemm_tile<C, kKind, kOutBf16, false>(g, m0, n0, lds);
+        gemm_tile<C, kKind, kOut, false>(g, m0, n0, lds);
     else
-        gemm_tile<C, kKind, kOutBf16, true>(g, m0, n0, lds);
+        gemm_tile<C, kKind, kOut, true>(g, m0, n0, lds);
 }
 
-template <class C, int kKind, bool kOutBf16>
+template <class C, int kKind, int kOut>
 hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const int64_t nb = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
     if (nb <= 0) return hipSuccess;
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     const size_t lds_bytes = (size_t)2 * (C::BM + C::BN) * BK * 2;
-    auto kern = gemm_kernel<C, kKind, kOutBf16>;
+    auto kern = gemm_kernel<C, kKind, kOut>;
     static bool attr_set = false;  // benign race: setting it twice is harmless
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
@@ -452,13 +562,19 @@ int tile_override() {
 
 template <class C, int kKind>
 hipError_t launch_out(const GemmArgs &g, int out_type, hipStream_t s) {
-    return out_type == OUT_BF16 ? launch_cfg<C, kKind, true>(g, s) : launch_cfg<C, kKind, false>(g, s);
+    if constexpr (kKind == KIND_NVFP4 && C::NT != 512)
+        if (out_type == OUT_NVFP4) return launch_cfg<C, kKind, OUT_NVFP4>(g, s);
+    if (out_type == OUT_NVFP4) return hipErrorInvalidValue;
+    return out_type == OUT_BF16 ? launch_cfg<C, kKind, OUT_BF16>(g, s) : launch_cfg<C, kKind, OUT_F32>(g, s);
 }
 
 template <int kKind>
 hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
     int t = tile_override();
     if (t == 0) t = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256 ? 2 : 3;
+    // the quantizing epilogue needs more registers than 8 waves leave the
+    // main loop: the 4-wave 256 x 256 tile (512 registers per lane) runs it
+    if (out_type == OUT_NVFP4 && t == 2) t = 1;
     if (t == 1) return launch_out<BigTile, kKind>(g, out_type, s);
     if (t == 2) return launch_out<BigTile8, kKind>(g, out_type, s);
     return launch_out<SmallTile, kKind>(g, out_type, s);
@@ -469,20 +585,28 @@ hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
 hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                              const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
                              int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, hipStream_t s) {
-    GemmArgs g{a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, 0, out, ld_out};
+    GemmArgs g{a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, 0, out, ld_out, nullptr, nullptr};
     return launch<KIND_NVFP4>(g, out_type, s);
+}
+
+hipError_t launch_gemm_nvfp4_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                                       const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                       int64_t M, int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales,
+                                       const float *y_alpha, hipStream_t s) {
+    GemmArgs g{a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, 0, y_codes, N / 2, y_scales, y_alpha};
+    return launch<KIND_NVFP4>(g, OUT_NVFP4, s);
 }
 
 hipError_t launch_gemm_fused(const uint16_t *x, int64_t ld_x, const float *a_alpha, const uint8_t *w_codes,
                              const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K,
                              void *out, int out_type, int64_t ld_out, hipStream_t s) {
-    GemmArgs g{x, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N, K, ld_x, out, ld_out};
+    GemmArgs g{x, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N, K, ld_x, out, ld_out, nullptr, nullptr};
     return launch<KIND_FUSED>(g, out_type, s);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
                             int out_type, int64_t ld_out, hipStream_t s) {
-    GemmArgs g{a, nullptr, nullptr, w, nullptr, nullptr, M, N, K, K, out, ld_out};
+    GemmArgs g{a, nullptr, nullptr, w, nullptr, nullptr, M, N, K, K, out, ld_out, nullptr, nullptr};
     return launch<KIND_BF16>(g, out_type, s);
 }
 

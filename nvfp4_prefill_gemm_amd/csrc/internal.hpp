@@ -20,12 +20,19 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_
 // alpha from partials only (fused path, dynamic mode).
 hipError_t launch_alpha_from_partials(const uint32_t *partials, int nparts, float *alpha, hipStream_t s);
 
-enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
+enum OutType { OUT_F32 = 0, OUT_BF16 = 1, OUT_NVFP4 = 2 };
 
 hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                              const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                              int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
                              hipStream_t s);
+
+// Tile GEMM whose epilogue quantizes Y to NVFP4 with a static tensor scale
+// (codes [M, N/2], scales [M, N/16]); N % 16 == 0, y_codes 4-byte aligned.
+hipError_t launch_gemm_nvfp4_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                                       const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                       int64_t M, int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales,
+                                       const float *y_alpha, hipStream_t s);
 
 hipError_t launch_gemm_fused(const uint16_t *x, int64_t ld_x, const float *a_alpha,
                              const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,

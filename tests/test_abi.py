@@ -79,6 +79,12 @@ def test_gemm_argument_errors(L):
     assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL  # null alpha
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL
     assert g(None, None, None, None, None, None, 0, 8, 32, None, 0, 8, None) == NVFP4_OK
+    q = L.nvfp4_gemm_quant_out
+    assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 24, 32, FAKE, FAKE, FAKE, None) == NVFP4_EINVAL  # N % 16
+    assert b"multiple of 16" in L.nvfp4_last_error()
+    assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 32, FAKE, FAKE, None, None) == NVFP4_EINVAL  # y_alpha
+    assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 32, ctypes.c_void_p(0x1002), FAKE, FAKE, None) == NVFP4_EINVAL
+    assert q(None, None, None, None, None, None, 0, 16, 32, None, None, None, None) == NVFP4_OK
     odd = ctypes.c_void_p(0x1002)
     assert g(FAKE, odd, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL  # scale align
     assert b"4-byte aligned" in L.nvfp4_last_error()

@@ -71,6 +71,23 @@ def test_static_alpha_and_strided_rows(nv, oracle_mod):
     _assert_same(_gpu_quant(nv, xb, ld=520), oracle_mod.quantize(xb), "strided")
 
 
+def test_static_alpha_extreme_quotients(nv, oracle_mod):
+    """Static tensor scales far below the data: block scales saturate at 448
+    and x / (alpha * sigma) exceeds 2^120 or overflows FP32 (codes clip to
+    +-6), next to ordinary blocks; and scales far above it (quotients that
+    underflow)."""
+    g = np.random.default_rng(21)
+    x = g.standard_normal((8, 256)).astype(np.float32)
+    x[0] *= np.float32(2.0 ** 120)
+    x[1] *= np.float32(2.0 ** 60)
+    x[2, :16] = np.float32(-3.0e38)
+    x[3] *= np.float32(2.0 ** -100)
+    xb = wl.to_bf16_bits(x)
+    for alpha in (2.0 ** -105, 2.0 ** -60, 1.0e-30, 2.0 ** 100):
+        say("quantize extreme static alpha", alpha)
+        _assert_same(_gpu_quant(nv, xb, alpha=alpha), oracle_mod.quantize(xb, alpha=alpha), f"extreme static {alpha}")
+
+
 def _special_tensor():
     """Zero blocks, signed zeros, E2M1 ties, tiny and saturating blocks (alpha = 1)."""
     rows = []
