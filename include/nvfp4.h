@@ -91,7 +91,7 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
  *   K % 16 == 0; M, N >= 0; code arrays 16-byte aligned, scale arrays 4-byte aligned
  *   out [M, ld_out] FP32 (NVFP4_OUT_F32) or BF16 (NVFP4_OUT_BF16, nearest-even),
  *   ld_out >= N.  Accumulation is FP32; each product q*sigma is exact.
- * At decode shapes (M <= 64, K % 32 == 0; the uniform-NVFP4 and FP4-decode
+ * At decode shapes (M <= 64, K % 32 == 0, K < 2^24; the uniform-NVFP4 and FP4-decode
  * variants of Mix-Quant Section 4) a split-K kernel streams the weights;
  * otherwise a tile kernel runs.  Both sum in FP32 but in different orders.
  */

@@ -107,7 +107,7 @@ int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_a
     if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
     if ((rc = check_nvfp4(a_codes, a_scales, a_alpha, "A", fn))) return rc;
     if ((rc = check_nvfp4(w_codes, w_scales, w_alpha, "W", fn))) return rc;
-    if (M <= nvfp4::kSkinnyMaxM && K % 32 == 0)
+    if (M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % 32 == 0)
         return hip_status(nvfp4::launch_skinny_nvfp4(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K,
                                                      out, out_dtype, ld_out, s),
                           "nvfp4 decode kernel");
@@ -199,7 +199,7 @@ int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int6
     if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
     if (!a_bf16 || !w_bf16) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
     if (!aligned(a_bf16, 16) || !aligned(w_bf16, 16)) return fail(NVFP4_EINVAL, "%s: A and W must be 16-byte aligned", fn);
-    if (M <= nvfp4::kSkinnyMaxM)
+    if (M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK)
         return hip_status(nvfp4::launch_skinny_bf16((const uint16_t *)a_bf16, (const uint16_t *)w_bf16, M, N, K, out,
                                                     out_dtype, ld_out, s),
                           "skinny bf16 kernel");

@@ -348,31 +348,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     };
     // Pipeline step kt computes on LDS buffer kt & 1.  Register stage `use`
     // holds step kt + 1 (loaded during the previous step) and is staged into
-    // buffer (kt + 1) & 1, one quarter per k16 MFMA group (A's blocks in the
-    // first two groups, W's in the last two).  Step kt + 2 is loaded into
-    // `fill` before any MFMA, so the loads have the whole step to land, and
-    // moved into `use` at the end of the step.
+    // buffer (kt + 1) & 1 over the first three k16 MFMA groups (A's blocks,
+    // then W's).  Step kt + 2 is loaded into `fill` before any MFMA, so the
+    // loads have the whole step to land, and moved into `use` at the end.
     Stage use, fill;
-    auto step = [&](int kt, bool do_store, bool do_load) __attribute__((always_inline)) {
+    // LDS hand-off: this wave's LDS reads and writes complete, then a plain
+    // barrier (register prefetches stay in flight across it)
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+        __builtin_amdgcn_s_barrier();
+    };
+    // The stores into the idle buffer finish by the third k16 group; the
+    // barrier then sits before the last group, whose fragments are already in
+    // registers, and the next step's first fragments are read under its MFMAs.
+    auto step = [&](int kt, bool do_store, bool do_load, bool has_next) __attribute__((always_inline)) {
         const int cur = kt & 1;
         if (do_load) {
             load_part(fill, kt + 2, 0);
             load_part(fill, kt + 2, 1);
         }
-        read_frags(cur, 0, af[0], bf[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
             if (do_store) {
                 if (ks == 0) store_q(use, cur ^ 1, std::integral_constant<int, 0>());
                 if (ks == 1) store_q(use, cur ^ 1, std::integral_constant<int, 1>());
-                if (ks == 2) store_q(use, cur ^ 1, std::integral_constant<int, 2>());
-                if (ks == 3) store_q(use, cur ^ 1, std::integral_constant<int, 3>());
+                if (ks == 2) {
+                    store_q(use, cur ^ 1, std::integral_constant<int, 2>());
+                    store_q(use, cur ^ 1, std::integral_constant<int, 3>());
+                }
+            }
+            if (ks == KS - 1 && has_next) {
+                lds_barrier();
+                read_frags(cur ^ 1, 0, af[0], bf[0]);
             }
             mfmas(af[ks & 1], bf[ks & 1]);
         }
         if (do_load) use = fill;
     };
+    static_assert(KS == 4, "stores are spread over the first three k16 groups");
 
     if (KT > 0) {
         load_part(use, 0, 0);
@@ -384,17 +398,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
         }
     }
     __syncthreads();
+    if (KT > 0) read_frags(0, 0, af[0], bf[0]);
     int kt = 0;
-    for (; kt + 2 < KT; ++kt) {
-        step(kt, true, true);
-        __syncthreads();
-    }
+    for (; kt + 2 < KT; ++kt) step(kt, true, true, true);
     if (kt + 1 < KT) {
-        step(kt, true, false);
-        __syncthreads();
+        step(kt, true, false, true);
         ++kt;
     }
-    if (kt < KT) step(kt, false, false);
+    if (kt < KT) step(kt, false, false, false);
 
     // epilogue: y = (acc * alphaA) * alphaW, stored FP32 or BF16 (nearest-even)
     float sa = 1.0f, sw = 1.0f;

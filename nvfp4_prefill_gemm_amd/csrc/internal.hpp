@@ -69,6 +69,9 @@ constexpr int64_t kFusedDecodeMaxElems = 16 * 12288;
 
 // Largest M routed to the skinny decode kernels by bf16_gemm and nvfp4_gemm.
 constexpr int64_t kSkinnyMaxM = 64;
+// The decode kernels address each operand through a buffer resource of fewer
+// than 2^31 bytes (64 rows of BF16), so they take K < kSkinnyMaxK.
+constexpr int64_t kSkinnyMaxK = int64_t(1) << 24;
 
 hipError_t launch_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                               uint8_t *scales, hipStream_t s);

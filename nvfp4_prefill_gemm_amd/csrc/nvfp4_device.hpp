@@ -188,6 +188,24 @@ __device__ __forceinline__ uint32_t quant8(const uint32_t w[4], float d) {
     return packed | signs;
 }
 
+// Raw buffer loads: a resource covers [base, base + bytes); loads at offsets
+// past the end return zeros without touching memory, so guarded loads need
+// no branch.  Word 3 of the resource is the gfx9-family default.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kBufOOB = 0x80000000u;  // an offset past every resource used here
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// kNt: non-temporal (streamed once, e.g. weights at decode shapes).
+template <bool kNt = false>
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNt ? 2 : 0));
+}
+template <bool kNt = false>
+__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNt ? 2 : 0);
+}
+
 // 8 E2M1 codes (one 32-bit word, element 0 in the low nibble) times sigma ->
 // 8 FP16 values, exactly.  The hardware converts FP4 pairs to FP16 with a
 // power-of-two scale of 2^8; sig2 holds sigma * 2^-8 in both halves, and one

@@ -87,37 +87,34 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
 #pragma unroll
         for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    const uint16_t *wr[NG];
-    bool wv[NG];
+    // buffer resources over this workgroup's weight rows and over X: rows past
+    // N or M and steps past K read zeros (offset beyond the resource)
+    const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
+    const rsrc_t wrs = make_rsrc(w + n0 * K, (uint32_t)(nrows * K * 2));
+    const rsrc_t xrs = make_rsrc(x, (uint32_t)(M * K * 2));
+    uint32_t wro[NG], xro[MG];  // byte offsets of this lane's rows
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        const int64_t n = n0 + j * 16 + (lane & 15);
-        wv[j] = n < N;
-        wr[j] = w + (wv[j] ? n : 0) * K;
-    }
-    const uint16_t *xr[MG];
-    bool xv[MG];
+    for (int j = 0; j < NG; ++j) wro[j] = (uint32_t)((j * 16 + (lane & 15)) * K * 2);
 #pragma unroll
-    for (int i = 0; i < MG; ++i) {
-        const int64_t m = i * 16 + (lane & 15);
-        xv[i] = m < M;
-        xr[i] = x + (xv[i] ? m : 0) * K;
-    }
+    for (int i = 0; i < MG; ++i) xro[i] = (uint32_t)((i * 16 + (lane & 15)) * K * 2);
 
-    for (int64_t ks0 = wave; ks0 < KS; ks0 += (int64_t)WAVES * U) {
-        uint4 bw[U][NG], ax[U][MG];
+    // Two register stages of U K-steps each: the loads of the next stage are
+    // issued before the MFMAs of the current one, so every wave keeps loads in
+    // flight while it computes.
+    typedef uint4 WStage[U][NG];
+    typedef uint4 XStage[U][MG];
+    auto load = [&](int64_t ks0, WStage &bw, XStage &ax) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = (ks0 + (int64_t)u * WAVES) * 32 + kq;
-            const bool kin = k + 8 <= K;
+            const bool kin = k + 8 <= K;  // also false past the last step
 #pragma unroll
-            for (int j = 0; j < NG; ++j)
-                bw[u][j] = (kin && wv[j]) ? load_nt16(wr[j] + k)
-                                          : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < NG; ++j) bw[u][j] = buf_load16(wrs, kin ? wro[j] + (uint32_t)(k * 2) : kBufOOB);
 #pragma unroll
-            for (int i = 0; i < MG; ++i)
-                ax[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint4 *>(xr[i] + k) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < MG; ++i) ax[u][i] = buf_load16(xrs, kin ? xro[i] + (uint32_t)(k * 2) : kBufOOB);
         }
+    };
+    auto compute = [&](const WStage &bw, const XStage &ax) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -127,6 +124,22 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u][i]),
                                                                         __builtin_bit_cast(bf16x8_t, bw[u][j]),
                                                                         acc[i][j], 0, 0, 0);
+    };
+    const int64_t stride = (int64_t)WAVES * U;
+    WStage bw0, bw1;
+    XStage ax0, ax1;
+    int64_t ks0 = wave;
+    load(ks0, bw0, ax0);
+    for (;;) {
+        const int64_t k1 = ks0 + stride;
+        load(k1, bw1, ax1);
+        compute(bw0, ax0);
+        if (k1 >= KS) break;
+        const int64_t k2 = k1 + stride;
+        load(k2, bw0, ax0);
+        compute(bw1, ax1);
+        if (k2 >= KS) break;
+        ks0 = k2;
     }
 
     tile_reduce<MG, NG, WAVES, kOutBf16>(acc, 1.0f, 1.0f, M, N, n0, out, ld_out);
@@ -171,29 +184,34 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
 #pragma unroll
         for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    const uint8_t *wcr[NG], *wsr[NG];
-    bool wv[NG];
+    // buffer resources over this workgroup's weight rows (and over A in global
+    // memory): rows past N or M and chunks past K read zeros
+    const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
+    const rsrc_t wcs = make_rsrc(wc + n0 * cb, (uint32_t)(nrows * cb));
+    const rsrc_t wss = make_rsrc(ws + n0 * sb, (uint32_t)(nrows * sb));
+    const rsrc_t xcs = make_rsrc(ac, (uint32_t)(M * cb));
+    const rsrc_t xss = make_rsrc(as, (uint32_t)(M * sb));
+    uint32_t wco[NG], wso[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-        const int64_t n = n0 + j * 16 + (lane & 15);
-        wv[j] = n < N;
-        wcr[j] = wc + (wv[j] ? n : 0) * cb;
-        wsr[j] = ws + (wv[j] ? n : 0) * sb;
+        wco[j] = (uint32_t)((j * 16 + (lane & 15)) * cb);
+        wso[j] = (uint32_t)((j * 16 + (lane & 15)) * sb);
     }
-    const uint8_t *xcr[MG], *xsr[MG];
+    uint32_t xco[MG], xso[MG];
     bool xv[MG];
 #pragma unroll
     for (int i = 0; i < MG; ++i) {
         const int64_t m = i * 16 + (lane & 15);
         xv[i] = m < M;
-        xcr[i] = ac + (xv[i] ? m : 0) * cb;
-        xsr[i] = as + (xv[i] ? m : 0) * sb;
+        xco[i] = (uint32_t)((xv[i] ? m : 0) * cb);
+        xso[i] = (uint32_t)((xv[i] ? m : 0) * sb);
     }
+    const uint8_t *lc = nullptr, *ls = nullptr;  // LDS copy of A (fused path)
     float alpha_a = 0.0f;
     if constexpr (kA != A_NVFP4) {
         // quantize the whole batch into LDS: codes [M][K/2], then scales [M][K/16]
         extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
-        uint8_t *lc = xlds, *ls = xlds + M * cb;
+        uint8_t *lcw = xlds, *lsw = xlds + M * cb;
         // 32-bit indexing: M * K <= kFusedDecodeMaxElems
         const uint32_t octs = (uint32_t)(K >> 3), total = (uint32_t)M * octs;  // total is even (K % 32 == 0)
         auto load_oct = [&](uint32_t o) __attribute__((always_inline)) {
@@ -233,37 +251,47 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha_a);
             if (o < total) {
                 const uint32_t r = o / octs, oc = o - r * octs;
-                *reinterpret_cast<uint32_t *>(lc + r * cb + oc * 4) = quant8(w4, bs.d);
-                if ((oc & 1) == 0) ls[r * sb + (oc >> 1)] = (uint8_t)bs.code;
+                *reinterpret_cast<uint32_t *>(lcw + r * cb + oc * 4) = quant8(w4, bs.d);
+                if ((oc & 1) == 0) lsw[r * sb + (oc >> 1)] = (uint8_t)bs.code;
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < MG; ++i) {
-            const int64_t m = i * 16 + (lane & 15);
-            xcr[i] = lc + (xv[i] ? m : 0) * cb;
-            xsr[i] = ls + (xv[i] ? m : 0) * sb;
-        }
+        lc = lcw;
+        ls = lsw;
     }
 
-    for (int64_t c0 = wave; c0 < KC; c0 += (int64_t)WAVES * U) {
+    // Two register stages of U chunks each, as in the BF16 decode kernel.
+    struct NStage {
         uint4 wq[U][NG], xq[U][MG];
         uint32_t wsc[U][NG], xsc[U][MG];
+    };
+    auto load = [&](int64_t c0, NStage &st) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = (c0 + (int64_t)u * WAVES) * 128 + kg;
             const bool kin = k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
+            const uint32_t kc = (uint32_t)(k >> 1), ksc = (uint32_t)(k >> 4);
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                wq[u][j] = (kin && wv[j]) ? load_nt16(wcr[j] + (k >> 1)) : make_uint4(0, 0, 0, 0);
-                wsc[u][j] = (kin && wv[j]) ? *reinterpret_cast<const uint16_t *>(wsr[j] + (k >> 4)) : 0u;
+                st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + kc : kBufOOB);
+                st.wsc[u][j] = buf_load2(wss, kin ? wso[j] + ksc : kBufOOB);
             }
 #pragma unroll
-            for (int i = 0; i < MG; ++i) {  // global memory, or LDS for the fused path
-                xq[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint4 *>(xcr[i] + (k >> 1)) : make_uint4(0, 0, 0, 0);
-                xsc[u][i] = (kin && xv[i]) ? *reinterpret_cast<const uint16_t *>(xsr[i] + (k >> 4)) : 0u;
+            for (int i = 0; i < MG; ++i) {
+                if constexpr (kA == A_NVFP4) {
+                    st.xq[u][i] = buf_load16(xcs, (kin & xv[i]) ? xco[i] + kc : kBufOOB);
+                    st.xsc[u][i] = buf_load2(xss, (kin & xv[i]) ? xso[i] + ksc : kBufOOB);
+                } else {  // LDS: clamp the address, zero by select
+                    const uint32_t kk = kin ? kc : 0u, kks = kin ? ksc : 0u;
+                    const uint4 q = *reinterpret_cast<const uint4 *>(lc + xco[i] + kk);
+                    const uint32_t sc = *reinterpret_cast<const uint16_t *>(ls + xso[i] + kks);
+                    st.xq[u][i] = (kin & xv[i]) ? q : make_uint4(0, 0, 0, 0);
+                    st.xsc[u][i] = (kin & xv[i]) ? sc : 0u;
+                }
             }
         }
+    };
+    auto compute = [&](const NStage &st) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -271,21 +299,36 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
                 half8_t b[NG];
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
-                    const uint4 q = wq[u][j];
+                    const uint4 q = st.wq[u][j];
                     const uint32_t w = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
-                    b[j] = expand8(w, e4m3_to_f16x2_over256(t < 2 ? (wsc[u][j] & 0xFFu) : (wsc[u][j] >> 8)));
+                    b[j] = expand8(w, e4m3_to_f16x2_over256(t < 2 ? (st.wsc[u][j] & 0xFFu) : (st.wsc[u][j] >> 8)));
                 }
 #pragma unroll
                 for (int i = 0; i < MG; ++i) {
-                    const uint4 q = xq[u][i];
+                    const uint4 q = st.xq[u][i];
                     const uint32_t xw = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
                     const half8_t a =
-                        expand8(xw, e4m3_to_f16x2_over256(t < 2 ? (xsc[u][i] & 0xFFu) : (xsc[u][i] >> 8)));
+                        expand8(xw, e4m3_to_f16x2_over256(t < 2 ? (st.xsc[u][i] & 0xFFu) : (st.xsc[u][i] >> 8)));
 #pragma unroll
                     for (int j = 0; j < NG; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
                 }
             }
+    };
+    const int64_t stride = (int64_t)WAVES * U;
+    NStage s0, s1;
+    int64_t c0 = wave;
+    load(c0, s0);
+    for (;;) {
+        const int64_t c1 = c0 + stride;
+        load(c1, s1);
+        compute(s0);
+        if (c1 >= KC) break;
+        const int64_t c2 = c1 + stride;
+        load(c2, s0);
+        compute(s1);
+        if (c2 >= KC) break;
+        c0 = c2;
     }
 
     tile_reduce<MG, NG, WAVES, kOutBf16>(acc, kA == A_NVFP4 ? *a_alpha : alpha_a, *w_alpha, M, N, n0, out, ld_out);
@@ -326,24 +369,28 @@ __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, 
 
 }  // namespace
 
-// NVFP4_SKINNY_CFG=<waves>x<unroll> overrides the decode kernel shape (tuning knob).
+// NVFP4_SKINNY_CFG=8|16 overrides the waves per workgroup of the BF16 decode
+// kernel with one column group (tuning knob; default 16).
 int skinny_cfg() {
     static int v = -1;
     if (v < 0) {
         const char *e = getenv("NVFP4_SKINNY_CFG");
-        v = !e ? 0 : !strcmp(e, "8x4") ? 1 : !strcmp(e, "16x4") ? 2 : !strcmp(e, "8x8") ? 4 : 0;
+        v = (e && !strcmp(e, "8")) ? 1 : 0;
     }
     return v;
 }
 
+// K-steps per register stage.  With one row group a single step per stage
+// (two steps in flight per wave) measured fastest on the Qwen3-8B decode
+// layers; more row groups take two.
+template <int MG>
+constexpr int skinny_u() { return MG == 1 ? 1 : 2; }
+
 template <int MG, int NG>
 hipError_t launch_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out, int out_type,
                      int64_t ld_out, hipStream_t s) {
-    switch (skinny_cfg()) {
-        case 1: return launch_cfg<MG, NG, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
-        case 4: return launch_cfg<MG, NG, 8, 8>(a, w, M, N, K, out, out_type, ld_out, s);
-        default: return launch_cfg<MG, NG, 16, 4>(a, w, M, N, K, out, out_type, ld_out, s);
-    }
+    if (skinny_cfg() == 1) return launch_cfg<MG, NG, 8, skinny_u<MG>()>(a, w, M, N, K, out, out_type, ld_out, s);
+    return launch_cfg<MG, NG, 16, skinny_u<MG>()>(a, w, M, N, K, out, out_type, ld_out, s);
 }
 
 // NVFP4_DECODE_NG=1|2|4 forces the number of 16-column groups per
@@ -367,8 +414,8 @@ hipError_t launch_mg_ng(const uint16_t *a, const uint16_t *w, int64_t M, int64_t
                         int out_type, int64_t ld_out, hipStream_t s) {
     int ng = decode_ng_knob();
     if (ng == 0) ng = MG == 1 ? 1 : N >= 16384 ? 4 : N >= 6144 ? 2 : 1;
-    if (ng == 4) return launch_cfg<MG, 4, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (ng == 2) return launch_cfg<MG, 2, 8, 4>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (ng == 4) return launch_cfg<MG, 4, 8, 2>(a, w, M, N, K, out, out_type, ld_out, s);
+    if (ng == 2) return launch_cfg<MG, 2, 8, 2>(a, w, M, N, K, out, out_type, ld_out, s);
     return launch_mg<MG, 1>(a, w, M, N, K, out, out_type, ld_out, s);
 }
 
@@ -387,10 +434,12 @@ hipError_t launch_nv_ng(const uint8_t *ac, const uint8_t *as, const float *aa_in
     float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
     int ng = decode_ng_knob();
     if (ng == 0) ng = MG == 4 && N >= 6144 ? 2 : 1;
+    if (MG == 4 && ng == 4) ng = 2;  // four row groups by four column groups exceed the register file
+    constexpr int U = MG == 1 ? 2 : 1;  // chunks per register stage
     switch (ng) {
-        case 2: return launch_nvfp4_cfg<MG, 2, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
-        case 4: return launch_nvfp4_cfg<MG, 4, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
-        default: return launch_nvfp4_cfg<MG, 1, 16, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
+        case 2: return launch_nvfp4_cfg<MG, 2, 8, U>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
+        case 4: return launch_nvfp4_cfg<MG, MG == 4 ? 2 : 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
+        default: return launch_nvfp4_cfg<MG, 1, 16, U>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
     }
 }
 
@@ -411,9 +460,9 @@ hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, 
                                void *out, int out_type, int64_t ld_out, hipStream_t s) {
     if (M > 16 || M * K > kFusedDecodeMaxElems) return hipErrorInvalidValue;
     if (dynamic)
-        return launch_nvfp4_cfg<1, 1, 16, 2, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M,
+        return launch_nvfp4_cfg<1, 1, 16, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M,
                                                              N, K, out, out_type, ld_out, s, x, ld_x);
-    return launch_nvfp4_cfg<1, 1, 16, 2, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
+    return launch_nvfp4_cfg<1, 1, 16, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
                                                         K, out, out_type, ld_out, s, x, ld_x);
 }
 
