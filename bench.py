@@ -10,9 +10,13 @@ once before timing (offline, as in a deployed prefill worker).
 The headline value is TFLOP/s including activation quantization:
 sum(2*M*N*K) / (time of the four quantize+GEMM pairs).  Alongside it the
 script times, outside the headline: the in-library BF16 GEMM at the same
-shapes (speedup), the fused quantize-in-GEMM path, the BF16 decode GEMMs at
-batch 1/8/64 on the same weights, and the oracle on the host cores on a
-bounded slice of the same workload.  Prints one JSON line.
+shapes (speedup), the same comparison at 512 / 2048 / 32768 tokens, the fused
+quantize-in-GEMM path, the NVFP4-output GEMM, the MXFP4 path, the BF16 and
+NVFP4 decode GEMMs at batch 1/8/64 on the same weights, and the oracle on the
+host cores on a bounded slice of the same workload.  Prints one JSON line.
+
+--workload selects other prefill shapes for the same measurement: Qwen3-8B
+at 32768 tokens with Student-t(4) activations, or Qwen3-32B at 16384 tokens.
 """
 from __future__ import annotations
 
@@ -40,6 +44,9 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--no-extras", action="store_true", help="only the headline NVFP4 prefill timing")
+    p.add_argument("--workload", default="qwen3_8b_m8192",
+                   choices=["qwen3_8b_m8192", "qwen3_8b_m32768_t4", "qwen3_32b_m16384"],
+                   help="prefill linears to time (default: Qwen3-8B at 8192 tokens, the headline)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle leg")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
@@ -122,7 +129,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda", 0)
-    w = wl.WORKLOADS["qwen3_8b_m8192"]
+    w = wl.WORKLOADS[args.workload]
+    headline = args.workload == "qwen3_8b_m8192"
     M = w.M
     t_setup = time.time()
 
@@ -143,6 +151,7 @@ def main():
         del a_bits, w_bits
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
+    print(f"bench: {w.name} inputs ready in {setup_s:.1f} s", file=sys.stderr, flush=True)
     flops_step = sum(wl.flops(M, L["N"], L["K"]) for L in layers)
 
     # ------------------------------------------------------- headline: NVFP4
@@ -197,8 +206,9 @@ def main():
     gu_flops = wl.flops(M, gu["N"], gu["K"])
     gu_tflops = gu_flops / (gu["gemm_us"] * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gu_tflops / F16_PEAK_TFLOPS, 4), "traffic": _traffic_from_profile(),
-                "kernel": "gemm_kernel<NVFP4> gate_up 8192x24576x4096 (FP16 MFMA on exact q*sigma)",
+                "frac": round(gu_tflops / F16_PEAK_TFLOPS, 4),
+                "traffic": _traffic_from_profile() if headline else None,
+                "kernel": f"gemm_kernel<NVFP4> gate_up {M}x{gu['N']}x{gu['K']} (FP16 MFMA on exact q*sigma)",
                 "frac_of_fp4_peak": round(gu_tflops / FP4_PEAK_TFLOPS, 4)}
 
     result = {
@@ -206,7 +216,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": w.name, "M": M, "linears": [[n, k, nn] for n, k, nn in w.linears],
-                   "activations": "N(0,1) with 0.5% channels x20, BF16", "weights": "N(0,0.02) BF16 -> NVFP4 offline",
+                   "activations": ("Student-t(nu=4), BF16" if w.act_dist == "student_t4"
+                                   else "N(0,1) with 0.5% channels x20, BF16"),
+                   "weights": "N(0,0.02) BF16 -> NVFP4 offline",
                    "alpha": "dynamic", "out_dtype": "bf16", "storage": "nvfp4 (e2m1 codes + e4m3 per 16 + fp32)"},
         "frac_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),
         "frac_f16_mfma_peak": round(value / F16_PEAK_TFLOPS, 4),
@@ -219,8 +231,10 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
+    print(f"bench: headline {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_extras:
-        result.update(extras(args, nv, wl, layers, M, flops_step, step_ms))
+        result.update(extras(args, nv, wl, layers, M, flops_step, step_ms, sweep=headline))
+        print("bench: extras done", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, wl, w)
@@ -228,7 +242,7 @@ def main():
     return 0
 
 
-def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
+def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms, sweep=False):
     import torch
 
     dev = torch.device("cuda", 0)
@@ -251,6 +265,54 @@ def extras(args, nv, wl, layers, M, flops_step, nvfp4_step_ms):
     bf16_ms = s.elapsed_time(e) / reps
     out["bf16_tflops"] = round(flops_step / (bf16_ms * 1e-3) / 1e12, 2)
     out["speedup_vs_bf16"] = round(bf16_ms / nvfp4_step_ms, 3)
+
+    # Phase-split sweep: NVFP4 prefill (dynamic-alpha quantizer + GEMM, BF16
+    # out) against the BF16 GEMM at other token counts, same weights; the
+    # activations are the first rows of the headline ones, or those rows
+    # repeated
+    if sweep:
+        def timed_ms(step):
+            for _ in range(2):
+                step()
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(reps):
+                step()
+            e.record()
+            torch.cuda.synchronize()
+            return s.elapsed_time(e) / reps
+
+        sw = {}
+        for Ms in wl.PHASE_SPLIT_PREFILL_M:
+            fl = sum(wl.flops(Ms, L["N"], L["K"]) for L in layers)
+            if Ms == M:
+                t4, t16 = nvfp4_step_ms, bf16_ms
+            else:
+                if Ms > M and Ms % M:
+                    continue
+                bufs = []
+                for L in layers:
+                    x = (L["x"][:Ms] if Ms <= M else L["x"].repeat(Ms // M, 1)).contiguous()
+                    bufs.append(dict(x=x, ac=torch.empty((Ms, L["K"] // 2), dtype=torch.uint8, device=dev),
+                                     asc=torch.empty((Ms, L["K"] // 16), dtype=torch.uint8, device=dev),
+                                     aal=torch.empty(1, dtype=torch.float32, device=dev),
+                                     wsb=torch.empty(max(nv.quantize_workspace_size(Ms, L["K"]), 4),
+                                                     dtype=torch.uint8, device=dev),
+                                     y=torch.empty((Ms, L["N"]), dtype=torch.bfloat16, device=dev)))
+
+                def nv_step():
+                    for L, B in zip(layers, bufs):
+                        nv.nvfp4_quantize(B["x"], B["ac"], B["asc"], B["aal"], workspace=B["wsb"])
+                        nv.nvfp4_gemm(B["ac"], B["asc"], B["aal"], L["wc"], L["ws"], L["wa"], out=B["y"])
+
+                def bf_step():
+                    for L, B in zip(layers, bufs):
+                        nv.bf16_gemm(B["x"], L["w_bf16"], out=B["y"])
+                t4, t16 = timed_ms(nv_step), timed_ms(bf_step)
+                del bufs
+            sw[str(Ms)] = {"nvfp4_tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
+                           "bf16_tflops": round(fl / (t16 * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(t16 / t4, 3)}
+        out["prefill_sweep"] = sw
 
     # fused quantize-in-GEMM prologue (dynamic alpha: amax pass + fused GEMM)
     def fused_step():

@@ -188,6 +188,34 @@ __device__ __forceinline__ uint32_t quant8(const uint32_t w[4], float d) {
     return packed | signs;
 }
 
+// quant8 on its fast path, with r = RN(1/d) supplied: for d in
+// [2^-90, 2^100] and every |x| <= d * 2^120, Markstein's correction on the
+// signed values with the sign of x OR-ed into the quotient (so -0 keeps code
+// 0x8), then the hardware convert, gives the codes of the IEEE quotient: a
+// CPU run over every finite BF16 numerator against 65536 such divisors found
+// no difference.  Numerators below 2^-100 need no special case: with
+// d >= 2^-90 their quotients stay far below 0.25, the first rounding step.
+__device__ __forceinline__ uint32_t quant8_fast(const uint32_t w[4], float d, float r) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        q[2 * i] = __uint_as_float(w[i] << 16);
+        q[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = q[i], q0 = x * r;
+        const float y = __builtin_fmaf(__builtin_fmaf(-q0, d, x), r, q0);
+        q[i] = __uint_as_float(__float_as_uint(y) | (__float_as_uint(x) & 0x80000000u));
+    }
+    uint32_t packed = 0;
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, q[0], q[1], 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, q[2], q[3], 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, q[4], q[5], 1.0f, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, q[6], q[7], 1.0f, 3);
+    return packed;
+}
+
 // Raw buffer loads: a resource covers [base, base + bytes); loads at offsets
 // past the end return zeros without touching memory, so guarded loads need
 // no branch.  Word 3 of the resource is the gfx9-family default.
@@ -204,6 +232,13 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
 template <bool kNt = false>
 __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNt ? 2 : 0);
+}
+
+__device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, off, 0, 0);
 }
 
 // 8 E2M1 codes (one 32-bit word, element 0 in the low nibble) times sigma ->

@@ -7,7 +7,9 @@
 //      lane takes 8 consecutive elements (one 16-byte load); lanes 2j and
 //      2j+1 share one 16-element block and exchange their half-block maxima
 //      with a DPP swap.  Codes leave as one 4-byte store per lane (coalesced),
-//      the E4M3 scale as one byte per lane pair.
+//      the E4M3 scale as one byte per lane pair.  The grid holds only as many
+//      workgroups as are resident at once; each wave walks its items with the
+//      next item's loads in flight.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -72,16 +74,35 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(const uint16_t 
     }
 }
 
-__device__ __forceinline__ float alpha_from_partials(const uint32_t *__restrict__ partials, int nparts) {
-    __shared__ uint32_t red[kWaves];
+// LDS hand-off that waits only for this wave's LDS operations, so global
+// loads already issued stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// This thread's share of the max over the amax partials (FP32 bits).
+__device__ __forceinline__ uint32_t partials_max(const uint32_t *__restrict__ partials, int nparts) {
     uint32_t m = 0;
     for (int i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partials[i]);
+    return m;
+}
+
+// alpha = amax / 2688 from every thread's partial max (workgroup-wide).
+__device__ __forceinline__ float alpha_from_max(uint32_t m) {
+    __shared__ uint32_t red[kWaves];
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
+    lds_barrier();
     uint32_t t = red[0];
     for (int i = 1; i < kWaves; ++i) t = max(t, red[i]);
     return div_rn(__uint_as_float(t), kAlphaDen);
+}
+
+__device__ __forceinline__ float alpha_from_partials(const uint32_t *__restrict__ partials, int nparts) {
+    return alpha_from_max(partials_max(partials, nparts));
 }
 
 __global__ __launch_bounds__(kThreads) void alpha_kernel(const uint32_t *__restrict__ partials, int nparts,
@@ -95,56 +116,116 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
                                                             int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
                                                             uint8_t *__restrict__ scales, float *__restrict__ alpha_io,
                                                             const uint32_t *__restrict__ partials, int nparts) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t octs = cols >> 3;  // 8-element groups per row; even, so pairs never straddle rows
-    const int64_t nseg = (octs + kSeg - 1) / kSeg;
-    const int64_t items = rows * nseg, stride = (int64_t)gridDim.x * kWaves;
-    auto load_item = [&](int64_t it, uint4 *v) __attribute__((always_inline)) {
-        const int64_t r = it / nseg, o0 = (it - r * nseg) * kSeg + lane;
-        const uint4 *xr = reinterpret_cast<const uint4 *>(x + r * ld);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // 32-bit item arithmetic: the host guarantees items < 2^31 and cols < 2^30
+    const uint32_t octs = (uint32_t)(cols >> 3);  // 8-element groups per row; even, so pairs never straddle rows
+    const uint32_t nseg = (octs + kSeg - 1) / kSeg;
+    const uint32_t items = (uint32_t)rows * nseg, nw = gridDim.x * kWaves;
+    // Every item is one wave's (row, segment): buffer resources over that row
+    // of X, codes and scales (empty past the last item) turn out-of-range
+    // loads into zeros and drop out-of-range stores, without branches.
+    auto load_item = [&](uint32_t it, uint4 *v) __attribute__((always_inline)) {
+        const bool ok = it < items;
+        const uint32_t r = ok ? it / nseg : 0u, o0 = (it - r * nseg) * kSeg + lane;
+        const rsrc_t xs = make_rsrc(x + (int64_t)r * ld, ok ? (uint32_t)cols * 2u : 0u);
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-            v[u] = (it < items && o0 + 64 * u < octs) ? load_nt16(xr + o0 + 64 * u) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kU; ++u) v[u] = buf_load16(xs, (o0 + 64u * u) * 16u);
     };
-    // the first item's loads are issued before the tensor scale is reduced
-    int64_t it = (int64_t)blockIdx.x * kWaves + wave;
-    uint4 v[kU];
-    load_item(it, v);
-    float alpha;
+    uint32_t it = blockIdx.x * kWaves + wave;
+    // the tensor scale's inputs are read first, then the first item's loads
+    // are issued, so waiting for the former leaves the latter in flight
+    // (nparts <= kMaxParts: at most kMaxParts / kThreads partials per thread,
+    // loaded without branches; entries past nparts read as zero)
+    constexpr int kPartsPerThread = kMaxParts / kThreads;
+    uint32_t pv[kPartsPerThread];
     if (kDynamic) {
-        alpha = alpha_from_partials(partials, nparts);
-        if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_io = alpha;
-    } else {
-        alpha = *alpha_io;
+        const rsrc_t ps = make_rsrc(partials, (uint32_t)nparts * 4u);
+#pragma unroll
+        for (int j = 0; j < kPartsPerThread; ++j)
+            pv[j] = __builtin_amdgcn_raw_buffer_load_b32(ps, (threadIdx.x + j * kThreads) * 4u, 0, 0);
     }
-    for (; it < items; it += stride) {
-        if (it != (int64_t)blockIdx.x * kWaves + wave) load_item(it, v);
-        const int64_t r = it / nseg, o0 = (it - r * nseg) * kSeg + lane;
-        uint32_t *cr = reinterpret_cast<uint32_t *>(codes + r * (cols >> 1));
-        uint8_t *sr = scales + r * (cols >> 4);
+    const float alpha_in = kDynamic ? 0.0f : *alpha_io;
+    asm volatile("" ::: "memory");
+    uint4 va[kU], vb[kU];
+    load_item(it, va);
+    float alpha = alpha_in;
+    if (kDynamic) {
+        uint32_t pmax = 0;
+#pragma unroll
+        for (int j = 0; j < kPartsPerThread; ++j) pmax = max(pmax, pv[j]);
+        alpha = alpha_from_max(pmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_io = alpha;
+    }
+    const float t = alpha * kQmax;
+    const float rt = t > 0.0f ? div_rn(1.0f, t) : 0.0f;
+    // Per E4M3 scale code: the divisor d = fl32(alpha * sigma), RN(1/d), and
+    // the largest |x| the fast path of quant8_fast takes (-1 when d is
+    // outside [2^-90, 2^100], zero included, so those blocks take quant8).
+    __shared__ float4 dtab[128];
+    if (threadIdx.x < 128) {
+        const float d = alpha * e4m3_decode(threadIdx.x);
+        const bool in = d >= 0x1p-90f && d <= 0x1p100f;
+        dtab[threadIdx.x] = make_float4(d, in ? div_rn(1.0f, d) : 0.0f, in ? d * 0x1p120f : -1.0f, 0.0f);
+    }
+    lds_barrier();
+    auto quant_item = [&](uint32_t it, const uint4 *v) __attribute__((always_inline)) {
+        const bool ok = it < items;
+        const uint32_t r = ok ? it / nseg : 0u, o0 = (it - r * nseg) * kSeg + lane;
+        const rsrc_t cs = make_rsrc(codes + (int64_t)r * (cols >> 1), ok ? (uint32_t)(cols >> 1) : 0u);
+        const rsrc_t ss = make_rsrc(scales + (int64_t)r * (cols >> 4), ok ? (uint32_t)(cols >> 4) : 0u);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t o = o0 + 64 * u;
+            const uint32_t o = o0 + 64u * u;
             const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
             uint32_t am = 0;  // bit pattern of max |x| over this lane's 8 elements
 #pragma unroll
             for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
             // partner lane (o ^ 1) holds the other half of the 16-element block
             const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
-            const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha);
-            if (o < octs) {
-                cr[o] = quant8(w, bs.d);
-                if ((o & 1) == 0) sr[o >> 1] = (uint8_t)bs.code;
-            }
+            const float amax_b = bf16_bits_to_f32(max(am, other));
+            const uint32_t code = e4m3_encode_sel(t > 0.0f ? div_rn_recip(amax_b, t, rt) : 0.0f);  // Eq. 3
+            const float4 e = dtab[code];
+            const uint32_t q = amax_b <= e.z ? quant8_fast(w, e.x, e.y) : quant8(w, e.x);  // Eq. 2
+            buf_store4(q, cs, o * 4u);
+            buf_store1(code, ss, (o & 1u) ? kBufOOB : o >> 1);
         }
+    };
+    // two register stages: the next item's loads are in flight while this
+    // one is quantized
+    for (;;) {
+        load_item(it + nw, vb);
+        quant_item(it, va);
+        it += nw;
+        if (it >= items) break;
+        load_item(it + nw, va);
+        quant_item(it, vb);
+        it += nw;
+        if (it >= items) break;
     }
 }
 
 int64_t quant_items(int64_t rows, int64_t cols) { return rows * (((cols >> 3) + kSeg - 1) / kSeg); }
 
+// Workgroups of the quantize kernel: one per 4 items, at most as many as the
+// device holds at once (each wave then loops over items with its loads
+// pipelined).
+template <bool kDynamic>
 int quant_grid(int64_t rows, int64_t cols) {
+    static int resident[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+    if (resident[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_kernel<kDynamic>, kThreads, 0) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 4;
+        resident[dev] = cus * per_cu;
+    }
     int64_t g = (quant_items(rows, cols) + kWaves - 1) / kWaves;
-    if (g > 65536) g = 65536;
+    if (g > resident[dev]) g = resident[dev];
     return (int)(g < 1 ? 1 : g);
 }
 
@@ -165,7 +246,8 @@ hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, i
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials, int nparts,
                            hipStream_t s) {
-    dim3 grid(quant_grid(rows, cols)), block(kThreads);
+    if (quant_items(rows, cols) >= (int64_t(1) << 31) || cols >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+    dim3 grid(dynamic ? quant_grid<true>(rows, cols) : quant_grid<false>(rows, cols)), block(kThreads);
     if (dynamic)
         hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, s, x, rows, cols, ld, codes, scales, alpha,
                            partials, nparts);
