@@ -196,10 +196,13 @@ __device__ __forceinline__ void bf16_store(const Bf16Stage<Part<R, NT>::EPT> &st
     for (int c = C0; c < C1; ++c) *reinterpret_cast<u32x4_t *>(lds + lds_off(r, c0 + c)) = st.v[c];
 }
 
-// Fused prologue: quantize the staged BF16 values exactly as the standalone
-// quantizer does (same block_scale / quant8), then expand q * sigma.
+// Fused prologue: quantize the staged BF16 values with the standalone
+// quantizer's arithmetic (Eq. 3 by the corrected quotient against
+// t = alpha * 6 with rt = RN(1/t); Eq. 2 by quant8_fast, or quant8 for a
+// block outside its range), then expand q * sigma.
 template <int R, int NT, int H = -1>
-__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, float alpha) {
+__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, float alpha, float t,
+                                            float rt) {
     constexpr int EPT = Part<R, NT>::EPT;
     constexpr int NB = EPT / 16, B0 = H < 0 ? 0 : H * NB / 2, B1 = H < 0 ? NB : (H + 1) * NB / 2;
     const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
@@ -210,11 +213,15 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
         uint32_t am = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-        const BlockScale bs = block_scale(bf16_bits_to_f32(am), alpha);
-        const half2_t s2 = e4m3_to_f16x2_over256(bs.code);
+        const float amax_b = bf16_bits_to_f32(am);
+        const uint32_t code = e4m3_encode_sel(t > 0.0f ? div_rn_recip(amax_b, t, rt) : 0.0f);
+        const float d = alpha * e4m3_decode(code);
+        const bool fast = d >= 0x1p-90f && d <= 0x1p100f && amax_b <= d * 0x1p120f;
+        const float rd = fast ? div_rn(1.0f, d) : 0.0f;
+        const half2_t s2 = e4m3_to_f16x2_over256(code);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint32_t packed = quant8(&w[4 * c], bs.d);
+            const uint32_t packed = fast ? quant8_fast(&w[4 * c], d, rd) : quant8(&w[4 * c], d);
             *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b + c)) = expand8(packed, s2);
         }
     }
@@ -269,8 +276,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     // row limits seen by the loaders: the real ones, or "infinite" on the fast path
 
-    float a_alpha = 1.0f;
-    if (kKind == KIND_FUSED) a_alpha = *g.a_alpha;
+    float a_alpha = 1.0f, a_t = 0.0f, a_rt = 0.0f;
+    if (kKind == KIND_FUSED) {
+        a_alpha = *g.a_alpha;
+        a_t = a_alpha * kQmax;
+        a_rt = a_t > 0.0f ? div_rn(1.0f, a_t) : 0.0f;
+    }
 
     typedef typename StageSel<kKind, Part<BM, NT>::EPT, Part<BN, NT>::EPT>::type Stage;
 
@@ -295,7 +306,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
         constexpr int h = q & 1;
         if constexpr (q < 2) {
             if constexpr (kKind == KIND_NVFP4) fp4_store<BM, NT, h>(st.a, (half_t *)As(s));
-            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT, h>(st.a, (half_t *)As(s), a_alpha);
+            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT, h>(st.a, (half_t *)As(s), a_alpha, a_t, a_rt);
             if constexpr (kKind == KIND_BF16) bf16_store<BM, NT, h>(st.a, (uint16_t *)As(s));
         } else {
             if constexpr (kKind == KIND_BF16)
@@ -588,9 +599,12 @@ template <int kKind>
 hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
     int t = tile_override();
     if (t == 0) t = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256 ? 2 : 3;
-    // the quantizing epilogue needs more registers than 8 waves leave the
-    // main loop: the 4-wave 256 x 256 tile (512 registers per lane) runs it
-    if (out_type == OUT_NVFP4 && t == 2) t = 1;
+    // the quantizing epilogue and the fused prologue need more registers
+    // than 8 waves leave the main loop (they spill there): the 4-wave
+    // 256 x 256 tile (512 registers per lane) runs them
+    // (the NVFP4-output epilogue is not built for 8 waves; the fused kind
+    // still takes an explicit NVFP4_GEMM_TILE=big8)
+    if (t == 2 && (out_type == OUT_NVFP4 || (kKind == KIND_FUSED && tile_override() == 0))) t = 1;
     if (t == 1) return launch_out<BigTile, kKind>(g, out_type, s);
     if (t == 2) return launch_out<BigTile8, kKind>(g, out_type, s);
     return launch_out<SmallTile, kKind>(g, out_type, s);
