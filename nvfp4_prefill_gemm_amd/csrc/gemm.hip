@@ -381,11 +381,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-            // NVFP4: keep the next group's fragment reads ahead of this
-            // group's MFMAs (the scheduler otherwise sinks each read next to
-            // its use and the LDS latency is exposed).  Measured slower for
-            // the BF16 and fused kinds, which keep the default schedule.
-            if constexpr (kKind == KIND_NVFP4) __builtin_amdgcn_sched_barrier(0);
+            // NVFP4 and fused: keep the next group's fragment reads ahead of
+            // this group's MFMAs (the scheduler otherwise sinks each read next
+            // to its use and the LDS latency is exposed).  Measured slower for
+            // the BF16 kind, which keeps the default schedule.
+            if constexpr (kKind != KIND_BF16) __builtin_amdgcn_sched_barrier(0);
             if (do_store) {
                 if (ks == 0) store_q(use, cur ^ 1, std::integral_constant<int, 0>());
                 if (ks == 1) store_q(use, cur ^ 1, std::integral_constant<int, 1>());

@@ -37,24 +37,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Eq. 3's projection onto the E4M3 grid: nearest-even, saturating at 448.
-// s >= 0.  Returns the 8-bit code (sign bit clear).
-__device__ __forceinline__ uint32_t e4m3_encode(float s) {
-    if (!(s < kE4M3Max)) return 0x7Eu;
-    if (s < 0.015625f) {
-        // below the smallest normal 2^-6: the grid is m * 2^-9, m = 0..8, and
-        // code m (m = 8 is the smallest normal, code 0x08).
-        return (uint32_t)__builtin_rintf(s * 512.0f);
-    }
-    uint32_t b = __float_as_uint(s);
-    // keep 3 mantissa bits, nearest-even; a carry moves into the exponent
-    uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
-    uint32_t code = r - ((127u - 7u) << 3);  // rebias 127 -> 7
-    return code > 0x7Eu ? 0x7Eu : code;
-}
-
-// e4m3_encode as selects instead of branches (identical codes for every
-// non-negative FP32 pattern, +inf and NaN included; checked exhaustively).
+// Eq. 3's projection onto the E4M3 grid: nearest-even, saturating at 448,
+// for s >= 0; returns the 8-bit code (sign bit clear).  Both candidate
+// encodings are formed and selected without branches: below the smallest
+// normal 2^-6 the grid is m * 2^-9 (m = 0..8, code m; m = 8 is the smallest
+// normal, code 0x08); above it 3 mantissa bits are kept, nearest-even, a
+// carry moving into the exponent, and the exponent rebiased 127 -> 7.
+// +inf and NaN give 0x7E.  (Checked exhaustively on the CPU against a
+// branch-per-case version over every non-negative FP32 pattern.)
 __device__ __forceinline__ uint32_t e4m3_encode_sel(float s) {
     const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
     const uint32_t b = __float_as_uint(s);
@@ -70,36 +60,8 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// Eq. 2's projection onto E2M1: nearest-even with clipping to +-6, sign of v
-// kept (so -0 and tiny negatives give 0x8).  Tie points 0.25, 0.75, 1.25,
-// 1.75, 2.5, 3.5, 5 go to the even mantissa.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-    float a = __builtin_fabsf(v);
-    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                 (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // Correctly rounded FP32 division (IEEE), independent of fast-math flags.
 __device__ __forceinline__ float div_rn(float x, float y) { return __fdiv_rn(x, y); }
-
-// One 16-element block: scale code and tensor-scaled divisor, from the block's
-// amax and the tensor scale alpha (Eq. 3).
-struct BlockScale {
-    uint32_t code;  // E4M3 code of sigma_b
-    float sigma;    // sigma_b
-    float d;        // fl32(alpha * sigma_b): the divisor of Eq. 2
-};
-__device__ __forceinline__ BlockScale block_scale(float amax_b, float alpha) {
-    float t = alpha * kQmax;
-    float s = (t > 0.0f) ? div_rn(amax_b, t) : 0.0f;
-    BlockScale r;
-    r.code = e4m3_encode(s);
-    r.sigma = e4m3_decode(r.code);
-    r.d = alpha * r.sigma;
-    return r;
-}
 
 // RN(a / d) for a >= 0 given r = RN(1/d), by Markstein's correction under the
 // conditions stated for quant8 below, else by the IEEE division.
@@ -109,29 +71,6 @@ __device__ __forceinline__ float div_rn_recip(float a, float d, float r) {
         return __builtin_fmaf(__builtin_fmaf(-q0, d, a), r, q0);
     }
     return div_rn(a, d);
-}
-
-// block_scale with t = fl32(alpha * 6) and rt = RN(1/t) supplied (the same
-// Eq. 3 result, one reciprocal per tensor instead of a division per block).
-__device__ __forceinline__ BlockScale block_scale_recip(float amax_b, float alpha, float t, float rt) {
-    const float s = (t > 0.0f) ? div_rn_recip(amax_b, t, rt) : 0.0f;
-    BlockScale r;
-    r.code = e4m3_encode(s);
-    r.sigma = e4m3_decode(r.code);
-    r.d = alpha * r.sigma;
-    return r;
-}
-
-// quant_elem with r = RN(1/d) supplied: the same code (sign of x kept).
-__device__ __forceinline__ uint32_t quant_elem_recip(float x, float d, float r) {
-    const float v = (d > 0.0f) ? div_rn_recip(fabsf(x), d, r) : 0.0f;
-    return e2m1_encode(v) | ((__float_as_uint(x) >> 28) & 8u);
-}
-
-// Eq. 2 for one element: code of x / d, or signed zero when d == 0.
-__device__ __forceinline__ uint32_t quant_elem(float x, float d) {
-    float v = (d > 0.0f) ? div_rn(x, d) : __uint_as_float(__float_as_uint(x) & 0x80000000u);
-    return e2m1_encode(v);
 }
 
 // Eq. 2 for 8 consecutive elements of one block: w[i] holds elements 2i
@@ -145,9 +84,10 @@ __device__ __forceinline__ uint32_t quant_elem(float x, float d) {
 // x == 0) and |x| <= d * 2^120 qualify (checked against the IEEE quotient on
 // 2.9e8 random BF16 and 2.5e8 random FP32 numerators on a CPU), and anything
 // else takes the IEEE division.  The magnitude is rounded to E2M1 by
-// the hardware FP32 -> FP4 convert (nearest-even with saturation; it agrees
-// with the compare ladder of e2m1_encode on every FP32 bit pattern) and the
-// sign is copied from x, which is the sign of x / d for d > 0.
+// the hardware FP32 -> FP4 convert (nearest-even with saturation at 6: it
+// agrees on every FP32 bit pattern with the ladder that counts the tie
+// points 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 passed, ties to the even
+// mantissa) and the sign is copied from x, which is the sign of x / d.
 __device__ __forceinline__ uint32_t quant8(const uint32_t w[4], float d) {
     uint32_t signs = 0;
 #pragma unroll
@@ -224,16 +164,12 @@ constexpr uint32_t kBufOOB = 0x80000000u;  // an offset past every resource used
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
-// kNt: non-temporal (streamed once, e.g. weights at decode shapes).
-template <bool kNt = false>
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNt ? 2 : 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-template <bool kNt = false>
 __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
-    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNt ? 2 : 0);
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
-
 __device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }

@@ -239,6 +239,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             alpha_a = div_rn(bf16_bits_to_f32(t), kAlphaDen);
             if (blockIdx.x == 0 && threadIdx.x == 0) *a_alpha = alpha_a;
         }
+        // Eq. 3 against t = alpha * 6 (one reciprocal per workgroup), Eq. 2 by
+        // quant8_fast, or quant8 for a block outside its range
+        const float at = alpha_a * kQmax, art = at > 0.0f ? div_rn(1.0f, at) : 0.0f;
         // thread pairs (t, t ^ 1) hold the two halves of a 16-element block
         for (uint32_t base = 0; base < total; base += WAVES * 64) {
             const uint32_t o = base + threadIdx.x;
@@ -248,11 +251,15 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
             const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
-            const BlockScale bs = block_scale(bf16_bits_to_f32(max(am, other)), alpha_a);
+            const float amax_b = bf16_bits_to_f32(max(am, other));
+            const uint32_t code = e4m3_encode_sel(at > 0.0f ? div_rn_recip(amax_b, at, art) : 0.0f);
+            const float d = alpha_a * e4m3_decode(code);
+            const bool fast = d >= 0x1p-90f && d <= 0x1p100f && amax_b <= d * 0x1p120f;
+            const uint32_t q = fast ? quant8_fast(w4, d, div_rn(1.0f, d)) : quant8(w4, d);
             if (o < total) {
                 const uint32_t r = o / octs, oc = o - r * octs;
-                *reinterpret_cast<uint32_t *>(lcw + r * cb + oc * 4) = quant8(w4, bs.d);
-                if ((oc & 1) == 0) lsw[r * sb + (oc >> 1)] = (uint8_t)bs.code;
+                *reinterpret_cast<uint32_t *>(lcw + r * cb + oc * 4) = q;
+                if ((oc & 1) == 0) lsw[r * sb + (oc >> 1)] = (uint8_t)code;
             }
         }
         __syncthreads();
