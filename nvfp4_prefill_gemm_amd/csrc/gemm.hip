@@ -79,6 +79,7 @@ struct GemmArgs {
     int64_t ld_out;
     uint8_t *out_scales;      // NVFP4 output: E4M3 block scales [M, N/16]
     const float *out_alpha;   // NVFP4 output: static tensor scale
+    int rows_rsrc = 0;        // edge tiles may address a tile's rows through one buffer resource (< 2^31 bytes)
 };
 
 // ---------------------------------------------------------------- loaders
@@ -101,14 +102,32 @@ struct Fp4Stage {
     uint32_t sc;  // EPT/16 scale bytes
 };
 
-template <int R, int NT, bool kGuard>
+// Operand loads per tile mode.  0 and 1 (K % 64 == 0, a tile's rows fit one
+// buffer resource): loads through a buffer resource over the tile's valid
+// rows, so rows past the matrix edge (mode 1) read zeros without branches;
+// buffer loads with 32-bit offsets also measured faster than global loads on
+// interior tiles (mode 0).  3: interior tile with plain global loads (the
+// fused kind, measured faster that way).  2: any tail, per-access checks.
+template <int R, int NT, int kMode>
 __device__ __forceinline__ void fp4_load(Fp4Stage<Part<R, NT>::EPT> &st, const uint8_t *__restrict__ codes,
                                          const uint8_t *__restrict__ scales, int64_t rows, int64_t K, int64_t row0,
                                          int kt) {
     constexpr int EPT = Part<R, NT>::EPT;
     const int64_t row = row0 + Part<R, NT>::row();
     const int64_t k0 = (int64_t)kt * BK + Part<R, NT>::part() * EPT;
-    if (!kGuard) {  // interior tile, K % 64 == 0: every access is in range
+    if (kMode <= 1) {
+        const int64_t nrows = rows - row0 < R ? rows - row0 : R;
+        const rsrc_t cs = make_rsrc(codes + row0 * (K >> 1), (uint32_t)(nrows * (K >> 1)));
+        const rsrc_t ss = make_rsrc(scales + row0 * (K >> 4), (uint32_t)(nrows * (K >> 4)));
+        const uint32_t rr = (uint32_t)Part<R, NT>::row();
+        const uint32_t co = rr * (uint32_t)(K >> 1) + (uint32_t)(k0 >> 1);
+#pragma unroll
+        for (int i = 0; i < EPT / 32; ++i) st.codes[i] = buf_load16(cs, co + 16 * i);
+        const uint32_t so = rr * (uint32_t)(K >> 4) + (uint32_t)(k0 >> 4);
+        st.sc = EPT == 64 ? buf_load4(ss, so) : buf_load2(ss, so);
+        return;
+    }
+    if (kMode == 3) {  // interior tile, K % 64 == 0: every access is in range
         const uint8_t *cp = codes + row * (K >> 1) + (k0 >> 1);
 #pragma unroll
         for (int i = 0; i < EPT / 32; ++i) st.codes[i] = *reinterpret_cast<const uint4 *>(cp + 16 * i);
@@ -169,13 +188,21 @@ struct Bf16Stage {
     u32x4_t v[EPT / 8];
 };
 
-template <int R, int NT, bool kGuard>
+template <int R, int NT, int kMode>
 __device__ __forceinline__ void bf16_load(Bf16Stage<Part<R, NT>::EPT> &st, const uint16_t *__restrict__ x, int64_t ld,
                                           int64_t rows, int64_t K, int64_t row0, int kt) {
     constexpr int EPT = Part<R, NT>::EPT;
     const int64_t row = row0 + Part<R, NT>::row();
     const int64_t k0 = (int64_t)kt * BK + Part<R, NT>::part() * EPT;
-    if (!kGuard) {  // interior tile, K % 64 == 0
+    if (kMode <= 1) {  // buffer resource over the valid rows (see fp4_load)
+        const int64_t nrows = rows - row0 < R ? rows - row0 : R;
+        const rsrc_t xs = make_rsrc(x + row0 * ld, (uint32_t)(nrows * ld * 2));
+        const uint32_t xo = ((uint32_t)Part<R, NT>::row() * (uint32_t)ld + (uint32_t)k0) * 2u;
+#pragma unroll
+        for (int c = 0; c < EPT / 8; ++c) st.v[c] = __builtin_bit_cast(u32x4_t, buf_load16(xs, xo + 16 * c));
+        return;
+    }
+    if (kMode == 3) {  // interior tile, K % 64 == 0
 #pragma unroll
         for (int c = 0; c < EPT / 8; ++c) st.v[c] = *reinterpret_cast<const u32x4_t *>(x + row * ld + k0 + 8 * c);
         return;
@@ -258,14 +285,19 @@ struct KindTraits<KIND_BF16> {
     typedef uint16_t lds_t;
 };
 
-// One output tile.  kGuard = false is the interior fast path (whole tile in
-// range and K % 64 == 0): no bounds checks, so each pipeline step is one
-// basic block the scheduler can interleave.  NVFP4 operands are prefetched
+// One output tile.  kMode 0 is the interior fast path (whole tile in range,
+// K % 64 == 0): no bounds checks, so each pipeline step is one basic block
+// the scheduler can interleave (mode 3: the same with global loads).  kMode 1
+// (a tile over the M or N edge) keeps
+// that shape, its loads reading zeros past the edge; the epilogue checks rows
+// and columns.  kMode 2 checks every access (K tails, or a tile whose rows
+// span 2^31 bytes or more).  NVFP4 operands are prefetched
 // two K steps ahead in registers (18 VGPRs a stage); BF16 operands one step.
-template <class C, int kKind, int kOut, bool kGuard>
+template <class C, int kKind, int kOut, int kMode>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t n0,
                                           typename KindTraits<kKind>::lds_t *lds) {
     typedef typename KindTraits<kKind>::lds_t lds_t;
+    constexpr bool kGuard = kMode == 1 || kMode == 2;  // the epilogue checks rows and columns
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, TM = C::TM, TN = C::TN;
     constexpr int KS = BK / 16;  // k16 MFMA steps per pipeline step
     auto As = [&](int s) __attribute__((always_inline)) { return lds + s * (BM + BN) * BK; };
@@ -289,14 +321,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     auto load_part = [&](Stage &st, int kt, int p) __attribute__((always_inline)) {
         if (p == 0) {
             if constexpr (kKind == KIND_NVFP4)
-                fp4_load<BM, NT, kGuard>(st.a, (const uint8_t *)g.a, g.a_scales, g.M, g.K, m0, kt);
+                fp4_load<BM, NT, kMode>(st.a, (const uint8_t *)g.a, g.a_scales, g.M, g.K, m0, kt);
             else
-                bf16_load<BM, NT, kGuard>(st.a, (const uint16_t *)g.a, g.lda, g.M, g.K, m0, kt);
+                bf16_load<BM, NT, kMode>(st.a, (const uint16_t *)g.a, g.lda, g.M, g.K, m0, kt);
         } else {
             if constexpr (kKind == KIND_BF16)
-                bf16_load<BN, NT, kGuard>(st.w, (const uint16_t *)g.w, g.K, g.N, g.K, n0, kt);
+                bf16_load<BN, NT, kMode>(st.w, (const uint16_t *)g.w, g.K, g.N, g.K, n0, kt);
             else
-                fp4_load<BN, NT, kGuard>(st.w, (const uint8_t *)g.w, g.w_scales, g.N, g.K, n0, kt);
+                fp4_load<BN, NT, kMode>(st.w, (const uint8_t *)g.w, g.w_scales, g.N, g.K, n0, kt);
         }
     };
     // stage quarter q of a register stage into LDS buffer s: A's first and
@@ -552,11 +584,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_kernel(GemmArgs g) {
     int tm, tn;
     tile_coords<C::BM, C::BN>(g.M, g.N, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-    const bool full = m0 + C::BM <= g.M && n0 + C::BN <= g.N && (g.K & (BK - 1)) == 0;
-    if (full)
-        gemm_tile<C, kKind, kOut, false>(g, m0, n0, lds);
-    else
-        gemm_tile<C, kKind, kOut, true>(g, m0, n0, lds);
+    if ((g.K & (BK - 1)) == 0 && g.rows_rsrc) {
+        if (m0 + C::BM <= g.M && n0 + C::BN <= g.N)
+            gemm_tile<C, kKind, kOut, kKind == KIND_FUSED ? 3 : 0>(g, m0, n0, lds);
+        else
+            gemm_tile<C, kKind, kOut, 1>(g, m0, n0, lds);
+    } else {
+        gemm_tile<C, kKind, kOut, 2>(g, m0, n0, lds);
+    }
 }
 
 template <class C, int kKind, int kOut>
@@ -566,13 +601,16 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     const size_t lds_bytes = (size_t)2 * (C::BM + C::BN) * BK * 2;
     auto kern = gemm_kernel<C, kKind, kOut>;
+    GemmArgs ga = g;
+    const int64_t a_row = kKind == KIND_NVFP4 ? g.K / 2 : g.lda * 2, w_row = kKind == KIND_BF16 ? g.K * 2 : g.K / 2;
+    ga.rows_rsrc = C::BM * a_row < (int64_t(1) << 31) && C::BN * w_row < (int64_t(1) << 31);
     static bool attr_set = false;  // benign race: setting it twice is harmless
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds_bytes, s, g);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds_bytes, s, ga);
     return hipGetLastError();
 }
 

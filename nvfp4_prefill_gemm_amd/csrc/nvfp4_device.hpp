@@ -167,6 +167,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
