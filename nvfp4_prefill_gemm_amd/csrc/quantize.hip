@@ -4,12 +4,11 @@
 //      writes one partial max |x| (as FP32 bits; non-negative floats order
 //      like their bit patterns, so an integer max is exact).
 //   2. quantize: every workgroup folds the partials into alpha, then each
-//      lane takes 8 consecutive elements (one 16-byte load); lanes 2j and
-//      2j+1 share one 16-element block and exchange their half-block maxima
-//      with a DPP swap.  Codes leave as one 4-byte store per lane (coalesced),
-//      the E4M3 scale as one byte per lane pair.  The grid holds only as many
-//      workgroups as are resident at once; each wave walks its items with the
-//      next item's loads in flight.
+//      lane takes whole 16-element blocks (two 16-byte loads each), so a
+//      block's amax and scale are formed once, in one lane.  Codes leave as
+//      one 8-byte store per block, the E4M3 scale as one byte.  The grid
+//      holds only as many workgroups as are resident at once; each wave
+//      walks its items with the next item's loads in flight.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -21,10 +20,12 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxParts = 1024;
 // Work item of both passes: kSeg 8-element groups (2048 elements) of one row,
-// kU 16-byte loads in flight per lane; short rows give one item each, long
-// rows several, so small batches still spread over many waves.
+// kU 16-byte loads per lane; short rows give one item each, long rows
+// several, so small batches still spread over many waves.
 constexpr int kU = 4;
 constexpr int64_t kSeg = 64 * kU;
+constexpr int kBlk = 2;  // quantize pass: 16-element blocks per lane and item (2048 elements)
+static_assert(kSeg * 8 == 64 * 16 * kBlk, "both passes share the item size");
 
 typedef __attribute__((ext_vector_type(2))) unsigned short ushort2_t;
 
@@ -125,12 +126,17 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     // Every item is one wave's (row, segment): buffer resources over that row
     // of X, codes and scales (empty past the last item) turn out-of-range
     // loads into zeros and drop out-of-range stores, without branches.
+    // Lane l of an item owns whole 16-element blocks: elements
+    // seg * 2048 + j * 1024 + 16 l .. + 16 for j = 0, 1 (two 16-byte loads each).
     auto load_item = [&](uint32_t it, uint4 *v) __attribute__((always_inline)) {
         const bool ok = it < items;
-        const uint32_t r = ok ? it / nseg : 0u, o0 = (it - r * nseg) * kSeg + lane;
+        const uint32_t r = ok ? it / nseg : 0u, e0 = (it - r * nseg) * (kSeg * 8) + lane * 16u;
         const rsrc_t xs = make_rsrc(x + (int64_t)r * ld, ok ? (uint32_t)cols * 2u : 0u);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) v[u] = buf_load16(xs, (o0 + 64u * u) * 16u);
+        for (int j = 0; j < kBlk; ++j) {
+            v[2 * j] = buf_load16(xs, (e0 + 1024u * j) * 2u);
+            v[2 * j + 1] = buf_load16(xs, (e0 + 1024u * j) * 2u + 16u);
+        }
     };
     uint32_t it = blockIdx.x * kWaves + wave;
     // the tensor scale's inputs are read first, then the first item's loads
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     }
     const float alpha_in = kDynamic ? 0.0f : *alpha_io;
     asm volatile("" ::: "memory");
-    uint4 va[kU], vb[kU];
+    uint4 va[2 * kBlk], vb[2 * kBlk];
     load_item(it, va);
     float alpha = alpha_in;
     if (kDynamic) {
@@ -171,24 +177,30 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     lds_barrier();
     auto quant_item = [&](uint32_t it, const uint4 *v) __attribute__((always_inline)) {
         const bool ok = it < items;
-        const uint32_t r = ok ? it / nseg : 0u, o0 = (it - r * nseg) * kSeg + lane;
+        const uint32_t r = ok ? it / nseg : 0u, e0 = (it - r * nseg) * (kSeg * 8) + lane * 16u;
         const rsrc_t cs = make_rsrc(codes + (int64_t)r * (cols >> 1), ok ? (uint32_t)(cols >> 1) : 0u);
         const rsrc_t ss = make_rsrc(scales + (int64_t)r * (cols >> 4), ok ? (uint32_t)(cols >> 4) : 0u);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const uint32_t o = o0 + 64u * u;
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            uint32_t am = 0;  // bit pattern of max |x| over this lane's 8 elements
+        for (int j = 0; j < kBlk; ++j) {
+            const uint32_t el = e0 + 1024u * j;
+            const uint32_t w[8] = {v[2 * j].x,     v[2 * j].y,     v[2 * j].z,     v[2 * j].w,
+                                   v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+            uint32_t am = 0;  // bit pattern of max |x| over the block
 #pragma unroll
-            for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-            // partner lane (o ^ 1) holds the other half of the 16-element block
-            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
-            const float amax_b = bf16_bits_to_f32(max(am, other));
+            for (int i = 0; i < 8; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+            const float amax_b = bf16_bits_to_f32(am);
             const uint32_t code = e4m3_encode_sel(t > 0.0f ? div_rn_recip(amax_b, t, rt) : 0.0f);  // Eq. 3
             const float4 e = dtab[code];
-            const uint32_t q = amax_b <= e.z ? quant8_fast(w, e.x, e.y) : quant8(w, e.x);  // Eq. 2
-            buf_store4(q, cs, o * 4u);
-            buf_store1(code, ss, (o & 1u) ? kBufOOB : o >> 1);
+            uint32_t lo, hi;  // Eq. 2
+            if (amax_b <= e.z) {
+                lo = quant8_fast(w, e.x, e.y);
+                hi = quant8_fast(w + 4, e.x, e.y);
+            } else {
+                lo = quant8(w, e.x);
+                hi = quant8(w + 4, e.x);
+            }
+            buf_store8(lo, hi, cs, el >> 1);
+            buf_store1(code, ss, el >> 4);
         }
     };
     // two register stages: the next item's loads are in flight while this

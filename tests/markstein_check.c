@@ -5,10 +5,11 @@
  *   codes <ND>: for ND divisors d spread over [2^-90, 2^100] and every finite
  *     BF16 numerator x with |x| <= d * 2^120, the E2M1 code (nearest-even
  *     ladder, clip to 6, sign kept) of
- *       q = fma(fma(-q0, d, x), r, q0) | sign(x),  r = RN(1/d), q0 = RN(x r)
- *     equals the code of the IEEE quotient RN(x / d).
+ *       q = fma(-fma(q0, d, -x), r, q0),  r = RN(1/d), q0 = RN(x r)
+ *     equals the code of the IEEE quotient RN(x / d), signed zeros included.
  *   quot <N>: for N random FP32 x in [2^-100, 2^127) and d in [2^-100, 2^100)
  *     with a normal finite quotient, the same q equals RN(x / d).
+ *   zeros: q of +0 and -0 keeps the sign for a spread of divisors.
  *
  * Prints the number of checked cases and mismatches; exits 1 on a mismatch. */
 #include <math.h>
@@ -26,10 +27,12 @@ static uint32_t e2m1(float v) {
   return c | ((ubits(v) >> 28) & 8u);
 }
 
+/* the residual is formed negated, e = RN(q0 d - x), and q = RN(q0 - e r):
+ * -0 then stays -0 (the usual order, RN(q0 + RN(x - q0 d) r), gives +0) */
 static float corrected(float x, float d, float r) {
   const float q0 = x * r;
-  const float q = fmaf(fmaf(-q0, d, x), r, q0);
-  return bits(ubits(q) | (ubits(x) & 0x80000000u));
+  const float e = fmaf(q0, d, -x);
+  return fmaf(-e, r, q0);
 }
 
 static uint64_t state = 88172645463325252ull;
@@ -70,6 +73,16 @@ int main(int argc, char **argv) {
       if (corrected(x, d, 1.0f / d) != ref) {
         if (bad < 5) printf("x=%a d=%a\n", x, d);
         ++bad;
+      }
+    }
+  } else if (!strcmp(argv[1], "zeros")) {
+    for (long long i = 0; i < n_arg; ++i) {
+      const float d = bits(((uint32_t)(127 - 90 + next() % 190) << 23) | (uint32_t)(next() & 0x7FFFFF));
+      for (int sgn = 0; sgn < 2; ++sgn) {
+        const float x = sgn ? -0.0f : 0.0f;
+        const float q = corrected(x, d, 1.0f / d);
+        ++n;
+        if (q != 0.0f || signbit(q) != signbit(x)) ++bad;
       }
     }
   } else {

@@ -2,8 +2,8 @@
 replace Eq. 2's per-element division (Mix-Quant Section 3.3, Eq. 2) by a
 reciprocal product with Markstein's correction: the E2M1 codes equal those of
 the IEEE quotient for every finite BF16 numerator over a spread of divisors,
-and the corrected quotient equals the IEEE quotient for random FP32
-numerators.  The kernels themselves are compared with the oracle bit for bit
+the corrected quotient equals the IEEE quotient for random FP32 numerators,
+and signed zeros keep their sign.  The kernels themselves are compared with the oracle bit for bit
 in the GPU tests; this pins the identity those kernels use, over far more
 cases than any GPU test covers."""
 import os
@@ -25,7 +25,7 @@ def checker(tmp_path_factory):
     return exe
 
 
-@pytest.mark.parametrize("mode,n", [("codes", 4096), ("quot", 50_000_000)])
+@pytest.mark.parametrize("mode,n", [("codes", 4096), ("quot", 50_000_000), ("zeros", 100_000)])
 def test_markstein_identity(checker, mode, n):
     r = subprocess.run([checker, mode, str(n)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
