@@ -77,6 +77,8 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
  *            NVFP4_ALPHA_STATIC mode (a tensor scale fixed ahead of time)
  *   workspace/workspace_bytes: see nvfp4_quantize_workspace_size
  * rows == 0 or cols == 0: nothing is launched (dynamic alpha is not written).
+ * cols >= 2^30 or rows * ceil(cols / 2048) >= 2^31: NVFP4_EUNSUPPORTED (the
+ * kernels index a row and the work items with 32-bit offsets).
  */
 int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
                    uint8_t *scales, float *alpha, int alpha_mode, void *workspace,

@@ -75,6 +75,8 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
     if (!aligned(x_bf16, 16)) return fail(NVFP4_EINVAL, "%s: x must be 16-byte aligned", fn);
     if (!aligned(codes, 16)) return fail(NVFP4_EINVAL, "%s: codes must be 16-byte aligned", fn);
     if (!aligned(alpha, 4)) return fail(NVFP4_EINVAL, "%s: alpha is misaligned", fn);
+    if (cols >= (int64_t(1) << 30) || rows * ((cols + 2047) / 2048) >= (int64_t(1) << 31))
+        return fail(NVFP4_EUNSUPPORTED, "%s: cols must be < 2^30 and rows * ceil(cols / 2048) < 2^31", fn);
     hipStream_t s = as_stream(stream);
     const int dyn = alpha_mode == NVFP4_ALPHA_DYNAMIC;
     const int nparts = nvfp4::amax_parts(rows, cols);

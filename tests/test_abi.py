@@ -67,6 +67,12 @@ def test_quantize_argument_errors(L):
     assert q(FAKE, 4, 32, 32, FAKE, FAKE, FAKE, 0, None, 0, None) == NVFP4_EWORKSPACE
     assert q(ctypes.c_void_p(0x1008), 4, 32, 32, FAKE, FAKE, FAKE, 1, None, 0, None) == NVFP4_EINVAL  # align
     assert q(None, 0, 32, 32, None, None, None, 0, None, 0, None) == NVFP4_OK  # empty: no launch
+    from nvfp4_prefill_gemm_amd.binding import NVFP4_EUNSUPPORTED
+
+    big = 1 << 30  # past the kernels' 32-bit row indexing
+    assert q(FAKE, 1, big, big, FAKE, FAKE, FAKE, 1, None, 0, None) == NVFP4_EUNSUPPORTED
+    assert b"2^30" in L.nvfp4_last_error()
+    assert q(FAKE, 1 << 31, 16, 16, FAKE, FAKE, FAKE, 1, None, 0, None) == NVFP4_EUNSUPPORTED  # items
 
 
 def test_gemm_argument_errors(L):
