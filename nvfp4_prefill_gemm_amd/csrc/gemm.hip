@@ -18,10 +18,13 @@
 // 512-thread workgroup, 2 x 4 waves of 128 x 64 (a 4 x 2 grid of 32x32x16
 // MFMAs each, 128 FP32 accumulators per lane; two waves per SIMD, so one
 // wave's staging work overlaps the other's MFMAs), K step 64 and a double-
-// buffered LDS stage of 2 x 64 KB; small problems a 128 x 128 tile of 4
-// waves of 64 x 64.  Operand fragments are read from LDS one k16 step ahead
+// buffered LDS stage of 2 x 64 KB; the NVFP4-output epilogue and the fused
+// prologue a 256 x 256 tile of 4 waves of 128 x 128 (their registers do not
+// fit beside 8 waves); small problems a 128 x 128 tile of 4 waves of
+// 64 x 64.  Operand fragments are read from LDS one k16 step ahead
 // of the MFMAs that use them; the next K step's global loads are issued
-// before the current step's MFMAs.  LDS rows are 64 halves = eight 16-byte
+// before the current step's MFMAs (through buffer resources: see the
+// loaders).  LDS rows are 64 halves = eight 16-byte
 // chunks, swizzled (lds_off) so operand reads and staging writes are free of
 // bank conflicts.
 #include <stdlib.h>
@@ -288,11 +291,10 @@ struct KindTraits<KIND_BF16> {
 // One output tile.  kMode 0 is the interior fast path (whole tile in range,
 // K % 64 == 0): no bounds checks, so each pipeline step is one basic block
 // the scheduler can interleave (mode 3: the same with global loads).  kMode 1
-// (a tile over the M or N edge) keeps
-// that shape, its loads reading zeros past the edge; the epilogue checks rows
-// and columns.  kMode 2 checks every access (K tails, or a tile whose rows
-// span 2^31 bytes or more).  NVFP4 operands are prefetched
-// two K steps ahead in registers (18 VGPRs a stage); BF16 operands one step.
+// (a tile over the M or N edge) keeps that shape, its loads reading zeros
+// past the edge; the epilogue checks rows and columns.  kMode 2 checks every
+// access (K tails, or a tile whose rows span 2^31 bytes or more).  Operands
+// are prefetched two K steps ahead in registers.
 template <class C, int kKind, int kOut, int kMode>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t n0,
                                           typename KindTraits<kKind>::lds_t *lds) {
@@ -306,7 +308,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     const int KT = (int)((g.K + BK - 1) / BK);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
-    // row limits seen by the loaders: the real ones, or "infinite" on the fast path
 
     float a_alpha = 1.0f, a_t = 0.0f, a_rt = 0.0f;
     if (kKind == KIND_FUSED) {

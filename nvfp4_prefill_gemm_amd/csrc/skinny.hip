@@ -5,9 +5,11 @@
 // from HBM: 2*N*K bytes against 2*M*N*K flops.  Each workgroup owns a strip
 // of NG*16 weight rows; its waves split K in 32-wide steps (interleaved, so
 // the waves of a workgroup read neighbouring 64-byte pieces of the same
-// rows), keep U steps of loads in flight, and run 16x16x32 BF16 MFMAs with
-// X zero-padded to MG*16 rows.  The per-wave partial tiles are summed
-// through LDS at the end.
+// rows), load through buffer resources over the valid rows (steps past K and
+// rows past N or M read zeros, so the loop has no branches), keep two
+// register stages of U steps in flight, and run 16x16x32 BF16 MFMAs with X
+// zero-padded to MG*16 rows.  The per-wave partial tiles are summed through
+// LDS at the end.
 //
 // NVFP4 (both operands E2M1 + E4M3 per 16, the uniform-NVFP4 and
 // FP4-decode variants of Mix-Quant's ablations, Section 4): the same split-K
