@@ -226,13 +226,23 @@ __device__ __forceinline__ void bf16_store(const Bf16Stage<Part<R, NT>::EPT> &st
     for (int c = C0; c < C1; ++c) *reinterpret_cast<u32x4_t *>(lds + lds_off(r, c0 + c)) = st.v[c];
 }
 
+// Per-workgroup constants of the fused prologue: the tensor scale, Eq. 3's
+// t = alpha * 6 with rt = RN(1/t) and the range where the corrected quotient
+// amax / t is exact, and per E4M3 code c the divisor d = alpha * sigma(c),
+// RN(1/d) and the largest amax the fast Eq. 2 path takes (-1 when d is
+// outside [2^-90, 2^100]).
+struct FusedQuant {
+    float alpha, t, rt, tlim;
+    bool tfast;
+    const float4 *dtab;
+};
+
 // Fused prologue: quantize the staged BF16 values with the standalone
-// quantizer's arithmetic (Eq. 3 by the corrected quotient against
-// t = alpha * 6 with rt = RN(1/t); Eq. 2 by quant8_fast, or quant8 for a
-// block outside its range), then expand q * sigma.
+// quantizer's arithmetic (Eq. 3 by the corrected quotient against t, else the
+// IEEE quotient; Eq. 2 by quant8_fast, or quant8 for a block outside its
+// range), then expand q * sigma.
 template <int R, int NT, int H = -1>
-__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, float alpha, float t,
-                                            float rt) {
+__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, const FusedQuant &fq) {
     constexpr int EPT = Part<R, NT>::EPT;
     constexpr int NB = EPT / 16, B0 = H < 0 ? 0 : H * NB / 2, B1 = H < 0 ? NB : (H + 1) * NB / 2;
     const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
@@ -240,18 +250,25 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
     for (int b = B0; b < B1; ++b) {
         const uint32_t w[8] = {st.v[2 * b].x, st.v[2 * b].y, st.v[2 * b].z, st.v[2 * b].w,
                                st.v[2 * b + 1].x, st.v[2 * b + 1].y, st.v[2 * b + 1].z, st.v[2 * b + 1].w};
-        uint32_t am = 0;
+        // block amax over the elements as FP32 (the values quant8_fast forms)
+        float amax_b = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-        const float amax_b = bf16_bits_to_f32(am);
-        const uint32_t code = e4m3_encode_sel(t > 0.0f ? div_rn_recip(amax_b, t, rt) : 0.0f);
-        const float d = alpha * e4m3_decode(code);
-        const bool fast = d >= 0x1p-90f && d <= 0x1p100f && amax_b <= d * 0x1p120f;
-        const float rd = fast ? div_rn(1.0f, d) : 0.0f;
+        for (int i = 0; i < 8; ++i)
+            amax_b = __builtin_fmaxf(amax_b, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w[i] << 16)),
+                                                             __builtin_fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+        float sq = 0.0f;  // Eq. 3
+        if (fq.t > 0.0f) {
+            const float q0 = amax_b * fq.rt;
+            sq = __builtin_fmaf(__builtin_fmaf(-q0, fq.t, amax_b), fq.rt, q0);
+            if (!(fq.tfast & (amax_b <= fq.tlim) & ((amax_b == 0.0f) | (amax_b >= 0x1p-100f))))
+                sq = div_rn(amax_b, fq.t);
+        }
+        const uint32_t code = e4m3_encode(sq);
+        const float4 e = fq.dtab[code];
         const half2_t s2 = e4m3_to_f16x2_over256(code);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint32_t packed = fast ? quant8_fast(&w[4 * c], d, rd) : quant8(&w[4 * c], d);
+            const uint32_t packed = amax_b <= e.z ? quant8_fast(&w[4 * c], e.x, e.y) : quant8(&w[4 * c], e.x);
             *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b + c)) = expand8(packed, s2);
         }
     }
@@ -309,11 +326,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-    float a_alpha = 1.0f, a_t = 0.0f, a_rt = 0.0f;
-    if (kKind == KIND_FUSED) {
-        a_alpha = *g.a_alpha;
-        a_t = a_alpha * kQmax;
-        a_rt = a_t > 0.0f ? div_rn(1.0f, a_t) : 0.0f;
+    FusedQuant fq{1.0f, 0.0f, 0.0f, 0.0f, false, nullptr};
+    if constexpr (kKind == KIND_FUSED) {
+        __shared__ float4 dtab[128];
+        fq.alpha = *g.a_alpha;
+        fq.t = fq.alpha * kQmax;
+        fq.rt = fq.t > 0.0f ? div_rn(1.0f, fq.t) : 0.0f;
+        fq.tfast = fq.t >= 0x1p-100f && fq.t <= 0x1p100f;
+        fq.tlim = fq.t * 0x1p120f;
+        fq.dtab = dtab;
+        if (threadIdx.x < 128) {
+            const float d = fq.alpha * e4m3_decode(threadIdx.x);
+            const bool in = d >= 0x1p-90f && d <= 0x1p100f;
+            dtab[threadIdx.x] = make_float4(d, in ? div_rn(1.0f, d) : 0.0f, in ? d * 0x1p120f : -1.0f, 0.0f);
+        }
+        __syncthreads();  // the table is read while the first stage is staged
     }
 
     typedef typename StageSel<kKind, Part<BM, NT>::EPT, Part<BN, NT>::EPT>::type Stage;
@@ -339,7 +366,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
         constexpr int h = q & 1;
         if constexpr (q < 2) {
             if constexpr (kKind == KIND_NVFP4) fp4_store<BM, NT, h>(st.a, (half_t *)As(s));
-            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT, h>(st.a, (half_t *)As(s), a_alpha, a_t, a_rt);
+            if constexpr (kKind == KIND_FUSED) fused_store<BM, NT, h>(st.a, (half_t *)As(s), fq);
             if constexpr (kKind == KIND_BF16) bf16_store<BM, NT, h>(st.a, (uint16_t *)As(s));
         } else {
             if constexpr (kKind == KIND_BF16)
@@ -519,7 +546,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
                 } else {
                     sq = t6 > 0.0f ? div_rn(amax, t6) : 0.0f;
                 }
-                const uint32_t code = e4m3_encode_sel(sq);
+                const uint32_t code = e4m3_encode(sq);
                 const float d = ya * e4m3_decode(code);
                 // Eq. 2: one reciprocal per block, Markstein per element
                 const float rd = d > 0.0f ? div_rn(1.0f, d) : 0.0f;

@@ -2,8 +2,8 @@
 //
 // NVFP4 (Mix-Quant, Section 3.3): E2M1 element codes, one FP8 E4M3 scale per
 // 16 elements, one FP32 tensor scale.  The rounding here is done with IEEE
-// bit manipulation and compare ladders; every function is round-to-nearest,
-// ties-to-even, on the FP32 value it is given.
+// bit manipulation and gfx950's FP4/FP8 converts; every function is
+// round-to-nearest, ties-to-even, on the FP32 value it is given.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,20 +38,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // Eq. 3's projection onto the E4M3 grid: nearest-even, saturating at 448,
-// for s >= 0; returns the 8-bit code (sign bit clear).  Both candidate
-// encodings are formed and selected without branches: below the smallest
-// normal 2^-6 the grid is m * 2^-9 (m = 0..8, code m; m = 8 is the smallest
-// normal, code 0x08); above it 3 mantissa bits are kept, nearest-even, a
-// carry moving into the exponent, and the exponent rebiased 127 -> 7.
-// +inf and NaN give 0x7E.  (Checked exhaustively on the CPU against a
-// branch-per-case version over every non-negative FP32 pattern.)
-__device__ __forceinline__ uint32_t e4m3_encode_sel(float s) {
-    const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
-    const uint32_t b = __float_as_uint(s);
-    uint32_t code = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
-    code = code > 0x7Eu ? 0x7Eu : code;
-    const uint32_t res = s < 0.015625f ? sub : code;
-    return !(s < kE4M3Max) ? 0x7Eu : res;
+// for s >= 0; returns the 8-bit code (sign bit clear).  gfx950's FP32 -> FP8
+// convert produces OCP E4M3 ("FN") with nearest-even rounding, subnormals
+// (the m * 2^-9 grid below 2^-6) included; the clamp to 448 first handles
+// saturation, and maps +inf and NaN (minNum) to 448, code 0x7E.  On the GPU
+// this agreed with a bit-manipulation encoder (3 mantissa bits kept, nearest-
+// even, a carry moving into the exponent; the subnormal grid by rint) on all
+// 2^31 non-negative FP32 bit patterns.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s, kE4M3Max), 0.0f, 0, false);
 }
 
 // E4M3 code (sign clear) -> FP32 value, exact.

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
 #pragma unroll
             for (int i = 0; i < 8; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
             const float amax_b = bf16_bits_to_f32(am);
-            const uint32_t code = e4m3_encode_sel(t > 0.0f ? div_rn_recip(amax_b, t, rt) : 0.0f);  // Eq. 3
+            const uint32_t code = e4m3_encode(t > 0.0f ? div_rn_recip(amax_b, t, rt) : 0.0f);  // Eq. 3
             const float4 e = dtab[code];
             uint32_t lo, hi;  // Eq. 2
             if (amax_b <= e.z) {

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
             const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
             const float amax_b = bf16_bits_to_f32(max(am, other));
-            const uint32_t code = e4m3_encode_sel(at > 0.0f ? div_rn_recip(amax_b, at, art) : 0.0f);
+            const uint32_t code = e4m3_encode(at > 0.0f ? div_rn_recip(amax_b, at, art) : 0.0f);
             const float d = alpha_a * e4m3_decode(code);
             const bool fast = d >= 0x1p-90f && d <= 0x1p100f && amax_b <= d * 0x1p120f;
             const uint32_t q = fast ? quant8_fast(w4, d, div_rn(1.0f, d)) : quant8(w4, d);

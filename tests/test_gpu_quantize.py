@@ -148,6 +148,27 @@ def test_dense_tie_neighbourhood(nv, oracle_mod):
     _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), "ties dynamic")
 
 
+def test_e4m3_scale_grid(nv, oracle_mod):
+    """Eq. 3 on every BF16 block amax from 2^-14 to 1024: with the static
+    tensor scale fl32(1/6), t = fl32(alpha * 6) is exactly 1, so s equals the
+    block amax and the E4M3 projection meets every tie and neighbour of the
+    normal and subnormal grids and the saturation at 448; the dynamic run
+    (tensor amax 1024) gives a non-power-of-two t."""
+    alpha = np.float32(1.0) / np.float32(6.0)
+    assert np.float32(alpha * np.float32(6.0)) == np.float32(1.0)
+    lo, hi = (int(b) for b in wl.to_bf16_bits(np.array([2.0 ** -14, 1024.0], dtype=np.float32)))
+    amax = wl.bf16_bits_to_f32(np.arange(lo, hi + 1, dtype=np.uint32).astype(np.uint16))
+    nb = -(-len(amax) // 16) * 16
+    amax = np.concatenate([amax, np.full(nb - len(amax), 1.0, dtype=np.float32)])
+    frac = np.array([1, -0.5, 1 / 3, -0.75, 0.25, 0, -0.125, 0.9, -0.6, 0.1, 0.05, -0.3, 0.7, -0.95, 0.2, 0.4],
+                    dtype=np.float32)
+    x = (amax[:, None] * frac[None, :]).reshape(nb // 16, 256)
+    xb = wl.to_bf16_bits(x)
+    say("quantize E4M3 scale grid", xb.shape)
+    _assert_same(_gpu_quant(nv, xb, alpha=float(alpha)), oracle_mod.quantize(xb, alpha=float(alpha)), "grid static")
+    _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), "grid dynamic")
+
+
 @pytest.mark.parametrize("layer", range(4))
 def test_qwen3_8b_m8192_full_tensors(nv, oracle_mod, layer):
     w = wl.WORKLOADS["qwen3_8b_m8192"]
