@@ -109,8 +109,9 @@ struct Fp4Stage {
 // buffer resource): loads through a buffer resource over the tile's valid
 // rows, so rows past the matrix edge (mode 1) read zeros without branches;
 // buffer loads with 32-bit offsets also measured faster than global loads on
-// interior tiles (mode 0).  3: interior tile with plain global loads (the
-// fused kind, measured faster that way).  2: any tail, per-access checks.
+// interior tiles (mode 0).  4: as 0, the scales supplied by the caller.
+// 3: interior tile with plain global loads (the fused kind, measured faster
+// that way).  2: any tail, per-access checks.
 template <int R, int NT, int kMode>
 __device__ __forceinline__ void fp4_load(Fp4Stage<Part<R, NT>::EPT> &st, const uint8_t *__restrict__ codes,
                                          const uint8_t *__restrict__ scales, int64_t rows, int64_t K, int64_t row0,
@@ -118,16 +119,18 @@ __device__ __forceinline__ void fp4_load(Fp4Stage<Part<R, NT>::EPT> &st, const u
     constexpr int EPT = Part<R, NT>::EPT;
     const int64_t row = row0 + Part<R, NT>::row();
     const int64_t k0 = (int64_t)kt * BK + Part<R, NT>::part() * EPT;
-    if (kMode <= 1) {
+    if (kMode <= 1 || kMode == 4) {  // 4: the scales come from the caller's per-group loads
         const int64_t nrows = rows - row0 < R ? rows - row0 : R;
         const rsrc_t cs = make_rsrc(codes + row0 * (K >> 1), (uint32_t)(nrows * (K >> 1)));
-        const rsrc_t ss = make_rsrc(scales + row0 * (K >> 4), (uint32_t)(nrows * (K >> 4)));
         const uint32_t rr = (uint32_t)Part<R, NT>::row();
         const uint32_t co = rr * (uint32_t)(K >> 1) + (uint32_t)(k0 >> 1);
 #pragma unroll
         for (int i = 0; i < EPT / 32; ++i) st.codes[i] = buf_load16(cs, co + 16 * i);
-        const uint32_t so = rr * (uint32_t)(K >> 4) + (uint32_t)(k0 >> 4);
-        st.sc = EPT == 64 ? buf_load4(ss, so) : buf_load2(ss, so);
+        if constexpr (kMode != 4) {
+            const rsrc_t ss = make_rsrc(scales + row0 * (K >> 4), (uint32_t)(nrows * (K >> 4)));
+            const uint32_t so = rr * (uint32_t)(K >> 4) + (uint32_t)(k0 >> 4);
+            st.sc = EPT == 64 ? buf_load4(ss, so) : buf_load2(ss, so);
+        }
         return;
     }
     if (kMode == 3) {  // interior tile, K % 64 == 0: every access is in range
@@ -276,6 +279,7 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
 
 // ---------------------------------------------------------------- kernel
 enum Kind { KIND_NVFP4 = 0, KIND_FUSED = 1, KIND_BF16 = 2 };
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 // Register stage of one pipeline step, per operand kind: A then W.
 template <class SA, class SW>
@@ -310,8 +314,10 @@ struct KindTraits<KIND_BF16> {
 // the scheduler can interleave (mode 3: the same with global loads).  kMode 1
 // (a tile over the M or N edge) keeps that shape, its loads reading zeros
 // past the edge; the epilogue checks rows and columns.  kMode 2 checks every
-// access (K tails, or a tile whose rows span 2^31 bytes or more).  Operands
-// are prefetched two K steps ahead in registers.
+// access (K tails, or a tile whose rows span 2^31 bytes or more).  kMode 4 is
+// mode 0 for NVFP4 operands with K % 256 == 0, the block scales fetched per
+// group of four K steps.  Operands are prefetched two K steps ahead in
+// registers.
 template <class C, int kKind, int kOut, int kMode>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t n0,
                                           typename KindTraits<kKind>::lds_t *lds) {
@@ -345,18 +351,53 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
 
     typedef typename StageSel<kKind, Part<BM, NT>::EPT, Part<BN, NT>::EPT>::type Stage;
 
+    // Mode 4 (NVFP4, two threads per row and step, K % 256 == 0): the block
+    // scales are fetched per group of four steps, 16 bytes per row (the
+    // row's two threads load 8 bytes each, one request) instead of 4 bytes
+    // per row and step; fetched per step they made half of the loop's L2
+    // requests.  A group is loaded two steps before its first fill and
+    // unpacked (each thread's 2 bytes of each step, half of them from the
+    // partner lane) when its first fill is issued.
+    constexpr bool kSB = kMode == 4;
+    static_assert(!kSB || (kKind == KIND_NVFP4 && Part<BM, NT>::EPT == 32 && Part<BN, NT>::EPT == 32 && BM == BN),
+                  "grouped scales: NVFP4, two threads per row");
+    // (resources over the tile's scale rows; built for every mode, used by 4)
+    const rsrc_t sra = make_rsrc(g.a_scales + m0 * (g.K >> 4), (uint32_t)(BM * (g.K >> 4)));
+    const rsrc_t srw = make_rsrc(g.w_scales + n0 * (g.K >> 4), (uint32_t)(BN * (g.K >> 4)));
+    const uint32_t sgo = (uint32_t)Part<BM, NT>::row() * (uint32_t)(g.K >> 4) + 8u * (uint32_t)Part<BM, NT>::part();
+    u32x2_t graw_a{0, 0}, graw_w{0, 0}, gpk_a{0, 0}, gpk_w{0, 0};
+    auto load_group = [&](int grp) __attribute__((always_inline)) {
+        graw_a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(sra, sgo, grp * 16, 0));
+        graw_w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(srw, sgo, grp * 16, 0));
+    };
+    // part 0 holds bytes 0-7 of the group (steps 0, 1), part 1 bytes 8-15;
+    // a part's 2 bytes of a step sit at 2 * part within the step's word
+    auto unpack = [&](u32x2_t v) __attribute__((always_inline)) {
+        const uint32_t ox = (uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+        const uint32_t oy = (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0xB1, 0xF, 0xF, false);
+        return (threadIdx.x & 1) ? u32x2_t{(ox >> 16) | (oy & 0xFFFF0000u), (v.x >> 16) | (v.y & 0xFFFF0000u)}
+                                 : u32x2_t{(v.x & 0xFFFFu) | (v.y << 16), (ox & 0xFFFFu) | (oy << 16)};
+    };
+    auto group_sc = [&](u32x2_t pk, int kt) __attribute__((always_inline)) {
+        return (((kt & 2) ? pk.y : pk.x) >> (16 * (kt & 1))) & 0xFFFFu;
+    };
+
     // load half p (0: A, 1: W) of pipeline step kt into the register stage
     auto load_part = [&](Stage &st, int kt, int p) __attribute__((always_inline)) {
         if (p == 0) {
-            if constexpr (kKind == KIND_NVFP4)
+            if constexpr (kKind == KIND_NVFP4) {
                 fp4_load<BM, NT, kMode>(st.a, (const uint8_t *)g.a, g.a_scales, g.M, g.K, m0, kt);
-            else
+                if constexpr (kSB) st.a.sc = group_sc(gpk_a, kt);
+            } else {
                 bf16_load<BM, NT, kMode>(st.a, (const uint16_t *)g.a, g.lda, g.M, g.K, m0, kt);
+            }
         } else {
-            if constexpr (kKind == KIND_BF16)
+            if constexpr (kKind == KIND_BF16) {
                 bf16_load<BN, NT, kMode>(st.w, (const uint16_t *)g.w, g.K, g.N, g.K, n0, kt);
-            else
+            } else {
                 fp4_load<BN, NT, kMode>(st.w, (const uint8_t *)g.w, g.w_scales, g.N, g.K, n0, kt);
+                if constexpr (kSB) st.w.sc = group_sc(gpk_w, kt);
+            }
         }
     };
     // stage quarter q of a register stage into LDS buffer s: A's first and
@@ -434,6 +475,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     // registers, and the next step's first fragments are read under its MFMAs.
     auto step = [&](int kt, bool do_store, bool do_load, bool has_next) __attribute__((always_inline)) {
         const int cur = kt & 1;
+        if constexpr (kSB) {
+            if (do_load && (kt & 3) == 0) load_group(min((kt >> 2) + 1, (KT >> 2) - 1));
+            if (do_load && (kt & 3) == 2) {
+                gpk_a = unpack(graw_a);
+                gpk_w = unpack(graw_w);
+            }
+        }
         if (do_load) {
             load_part(fill, kt + 2, 0);
             load_part(fill, kt + 2, 1);
@@ -464,6 +512,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
     };
     static_assert(KS == 4, "stores are spread over the first three k16 groups");
 
+    if constexpr (kSB) {
+        load_group(0);
+        gpk_a = unpack(graw_a);
+        gpk_w = unpack(graw_w);
+    }
     if (KT > 0) {
         load_part(use, 0, 0);
         load_part(use, 0, 1);
@@ -613,8 +666,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_kernel(GemmArgs g) {
     tile_coords<C::BM, C::BN>(g.M, g.N, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     if ((g.K & (BK - 1)) == 0 && g.rows_rsrc) {
-        if (m0 + C::BM <= g.M && n0 + C::BN <= g.N)
-            gemm_tile<C, kKind, kOut, kKind == KIND_FUSED ? 3 : 0>(g, m0, n0, lds);
+        if (m0 + C::BM <= g.M && n0 + C::BN <= g.N) {
+            if constexpr (kKind == KIND_NVFP4 && Part<C::BM, C::NT>::EPT == 32) {
+                if ((g.K & 255) == 0)
+                    gemm_tile<C, kKind, kOut, 4>(g, m0, n0, lds);
+                else
+                    gemm_tile<C, kKind, kOut, 0>(g, m0, n0, lds);
+            } else {
+                gemm_tile<C, kKind, kOut, kKind == KIND_FUSED ? 3 : 0>(g, m0, n0, lds);
+            }
+        }
         else
             gemm_tile<C, kKind, kOut, 1>(g, m0, n0, lds);
     } else {

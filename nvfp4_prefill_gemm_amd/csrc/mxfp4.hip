@@ -11,11 +11,10 @@
 // combine their maxima with two DPP swaps.
 //
 // GEMM: 256 x 256 output tile, 8 waves of 128 x 64 (4 x 2 scaled MFMAs of
-// 32x32x64), K step 256 (128 bytes of codes per row, the same LDS row shape
-// and swizzle as the FP16 GEMM), two LDS stages of 68 KB.  Interior steps
-// are staged with direct global -> LDS loads (global_load_lds_dwordx4: no
-// registers, no ALU; scales 4 bytes per lane); row and K tails with guarded
-// register loads.
+// 32x32x64).  Interior tiles with K % 512 == 0 run a register-staged
+// pipeline with K step 128 and block scales fetched per group of four steps
+// (mx_tile_pipe); edge tiles and other K a simpler loop with K step 256, two
+// LDS stages of 68 KB staged through guarded register loads (mx_tile_staged).
 #include <stdlib.h>
 #include <string.h>
 
@@ -86,6 +85,7 @@ constexpr int MBM = 256, MBN = 256, MNT = 512;
 constexpr int MWGN = 4;                // waves along N (2 along M)
 constexpr int MWM = 128, MWN = 64;     // wave tile
 constexpr int MTM = MWM / 32, MTN = MWN / 32;
+// the K-256 loop of edge tiles
 constexpr int MKB = 128;               // code bytes per row per step (256 k)
 constexpr int MKS = MKB / 32;          // 32x32x64 MFMA k-substeps per step
 constexpr int CODE_TILE = MBM * MKB;   // 32 KB
@@ -102,44 +102,222 @@ struct MxArgs {
 
 __device__ __forceinline__ int code_off(int row, int chunk) { return row * MKB + ((chunk ^ lds_swz(row)) << 4); }
 
-// Direct global -> LDS staging of one step (interior rows, whole step in K).
-// Code tiles: each wave instruction fills 1 KB = 8 rows; lane l writes slot
-// l % 8 of row l / 8, so it fetches logical chunk slot ^ f(row).
-__device__ __forceinline__ void stage_direct(const MxArgs &g, uint8_t *stage, int64_t m0, int64_t n0, int kt) {
+// Pipelined interior tiles (K % 512 == 0): K step 128, two LDS stages of A
+// and W codes (256 rows x 64 bytes each, swizzled 16-byte chunks), and the
+// scales in groups of four steps (16 bytes per row: K 512), two group buffers
+// of 8 KB.  Every fragment read is a register base plus an immediate offset.
+// Operands are staged through registers from buffer loads: step kt + 2 is
+// loaded while step kt computes, and step kt + 1 (loaded one step earlier) is
+// written to LDS between the two k64 sub-steps; the step's one barrier
+// follows, and the next step's fragments and scales are read under the second
+// sub-step's MFMAs.  A row's scales are fetched 16 bytes at a time, once per
+// four steps: fetched per step (4 bytes per row), they made half of the L2
+// requests of the loop for 6% of its bytes.
+constexpr int PKB = 64;                    // code bytes per row per step (128 k)
+constexpr int PCODE = MBM * PKB;           // 16 KB
+constexpr int PW = 2 * PCODE;              // W code stages
+constexpr int PSC = 4 * PCODE;             // scale groups: [2][A 256 x 16 B, W 256 x 16 B]
+constexpr int PSG = 2 * MBM * 16;          // 8 KB per group
+static_assert(PSC + 2 * PSG <= 2 * STAGE, "the pipelined stages fit the kernel's LDS");
+
+// 16-byte chunk c (of 4) of row r: slot c ^ ((r / 4) % 4), so the 16 rows a
+// quarter-wave reads at one chunk fall on distinct banks
+__device__ __forceinline__ int pcode_off(int row, int chunk) { return row * PKB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// one step's codes in registers: two 16-byte chunks of A and of W (native
+// vectors: HIP's uint4 wrapper kept these in scratch)
+struct MxRegs {
+    u32x4_t a0, a1, w0, w1;
+};
+
+template <bool kOutBf16>
+__device__ __forceinline__ void mx_store(const MxArgs &g, const f32x16_t (&acc)[MTM][MTN], int64_t m0, int64_t n0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t rb = g.K >> 1, sb = g.K >> 5;
+    const int wm = wave / MWGN, wn = wave % MWGN;
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-        const uint8_t *src = op ? g.wc : g.ac;
-        const int64_t row0 = op ? n0 : m0;
-        uint8_t *dst = stage + op * CODE_TILE;
+    for (int i = 0; i < MTM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int base = wave * 32 + q * 8;  // first tile row of this instruction
-            const int r = base + (lane >> 3), slot = lane & 7;
-            const int chunk = slot ^ lds_swz(r);
-            const uint8_t *gp = src + (row0 + r) * rb + (int64_t)kt * MKB + chunk * 16;
-            __builtin_amdgcn_global_load_lds(gp, dst + base * MKB, 16, 0, 0);
+        for (int j = 0; j < MTN; ++j) {
+            const int64_t col = n0 + wn * MWN + j * 32 + (lane & 31);
+            if (col >= g.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * MWM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row >= g.M) continue;
+                if (kOutBf16)
+                    reinterpret_cast<__bf16 *>(g.out)[row * g.ld_out + col] = (__bf16)acc[i][j][r];
+                else
+                    reinterpret_cast<float *>(g.out)[row * g.ld_out + col] = acc[i][j][r];
+            }
         }
-    }
-    // scales: 8 bytes per row = two dwords; waves 0-3 stage A's 512 dwords,
-    // waves 4-7 W's, 64 dwords (32 rows) per instruction
-    {
-        const int op = wave >> 2;
-        const uint8_t *src = op ? g.ws : g.as;
-        const int64_t row0 = op ? n0 : m0;
+}
+
+// k64 sub-step ks of a step: 4 x 2 scaled MFMAs; the lane's scale is byte 2 ks
+// of its (shifted) scale word
+__device__ __forceinline__ void mx_mfmas(f32x16_t (&acc)[MTM][MTN], const uint4 *fa, const uint4 *fb,
+                                         const uint32_t *sa, const uint32_t *sw, int ks) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int base = (wave & 3) * 128 + q * 64;  // first dword of this instruction
-            const int idx = base + lane, r = idx >> 1;
-            const uint8_t *gp = src + (row0 + r) * sb + (int64_t)kt * 8 + (idx & 1) * 4;
-            __builtin_amdgcn_global_load_lds(gp, stage + 2 * CODE_TILE + op * SCALE_TILE + base * 4, 4, 0, 0);
+    for (int i = 0; i < MTM; ++i) {
+        const i32x8_t a8 = {(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < MTN; ++j) {
+            const i32x8_t b8 = {(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0};
+            if (ks)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 2, (int)sa[i], 2,
+                                                                            (int)sw[j]);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0, (int)sa[i], 0,
+                                                                            (int)sw[j]);
         }
     }
 }
 
-// Guarded staging through registers: rows past M/N repeat the last row, code
-// chunks past K are zero and their scales 1.0 (code 127).
+template <bool kOutBf16>
+__device__ __forceinline__ void mx_tile_pipe(const MxArgs &g, uint8_t *smem, int64_t m0, int64_t n0) {
+    const int lane = threadIdx.x & 63, t = threadIdx.x;
+    const int wave = t >> 6;
+    const int wm = wave / MWGN, wn = wave % MWGN;
+    const int KT = (int)(g.K / 128);  // a multiple of 4
+    const uint32_t rb = (uint32_t)(g.K >> 1), sb = (uint32_t)(g.K >> 5);
+
+    // staging: thread t moves chunks t and t + 512 of each code tile (row
+    // i / 4, chunk i % 4) and, once per group, the 16 scale bytes of row t of
+    // A (t < 256) or t - 256 of W; buffer resources over the tile's rows, the
+    // step as the scalar offset
+    const rsrc_t ra_ = make_rsrc(g.ac + m0 * (int64_t)rb, MBM * rb);
+    const rsrc_t rw_ = make_rsrc(g.wc + n0 * (int64_t)rb, MBN * rb);
+    const int sop = t >> 8, sr = t & 255;
+    const rsrc_t rs_ = make_rsrc(sop ? g.ws + n0 * (int64_t)sb : g.as + m0 * (int64_t)sb, MBM * sb);
+    uint32_t go[2];
+    int lo[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = t + q * 512, r = i >> 2, c = i & 3;
+        go[q] = r * rb + c * 16;
+        lo[q] = pcode_off(r, c);
+    }
+    const uint32_t gso = sr * sb;
+    const int slo = PSC + sop * (MBM * 16) + sr * 16;
+    auto load_regs = [&](MxRegs &R, int kt) __attribute__((always_inline)) {
+        const int o = kt * PKB;
+        R.a0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra_, go[0], o, 0));
+        R.a1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra_, go[1], o, 0));
+        R.w0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw_, go[0], o, 0));
+        R.w1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw_, go[1], o, 0));
+    };
+    auto store_regs = [&](const MxRegs &R, int b) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4_t *>(smem + b * PCODE + lo[0]) = R.a0;
+        *reinterpret_cast<u32x4_t *>(smem + b * PCODE + lo[1]) = R.a1;
+        *reinterpret_cast<u32x4_t *>(smem + PW + b * PCODE + lo[0]) = R.w0;
+        *reinterpret_cast<u32x4_t *>(smem + PW + b * PCODE + lo[1]) = R.w1;
+    };
+    auto load_scales = [&](int grp) __attribute__((always_inline)) {
+        return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_, gso, grp * 16, 0));
+    };
+    auto store_scales = [&](u32x4_t v, int gb) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4_t *>(smem + slo + gb * PSG) = v;
+    };
+
+    // fragment and scale addresses of this lane: fragment i of A is 32 i rows
+    // further (same swizzle), the second k64 sub-step two chunks further
+    const int ra = wm * MWM + (lane & 31), rw = wn * MWN + (lane & 31);
+    const uint8_t *fa0 = smem + pcode_off(ra, lane >> 5), *fa1 = smem + (pcode_off(ra, lane >> 5) ^ 32);
+    const uint8_t *fb0 = smem + PW + pcode_off(rw, lane >> 5), *fb1 = smem + PW + (pcode_off(rw, lane >> 5) ^ 32);
+    const uint8_t *sca = smem + PSC + ra * 16, *scw = smem + PSC + MBM * 16 + rw * 16;
+    const int sh = 8 * (lane >> 5);  // upper half-wave: the odd 32-block of each k64
+    auto read_frags = [&](int b, int ks, uint4 *fa, uint4 *fb) __attribute__((always_inline)) {
+        const uint8_t *pa = (ks ? fa1 : fa0) + b * PCODE, *pb = (ks ? fb1 : fb0) + b * PCODE;
+#pragma unroll
+        for (int i = 0; i < MTM; ++i) fa[i] = *reinterpret_cast<const uint4 *>(pa + i * 32 * PKB);
+#pragma unroll
+        for (int j = 0; j < MTN; ++j) fb[j] = *reinterpret_cast<const uint4 *>(pb + j * 32 * PKB);
+    };
+    // step kt's scale words (word kt % 4 of the group's 16 bytes) as stored;
+    // shifted for the lane when the step starts, so the reads have a sub-step
+    // of MFMAs to land
+    auto read_scales = [&](int kt, uint32_t *sa, uint32_t *sw) __attribute__((always_inline)) {
+        const int o = ((kt >> 2) & 1) * PSG + (kt & 3) * 4;
+#pragma unroll
+        for (int i = 0; i < MTM; ++i) sa[i] = *reinterpret_cast<const uint32_t *>(sca + o + i * 32 * 16);
+#pragma unroll
+        for (int j = 0; j < MTN; ++j) sw[j] = *reinterpret_cast<const uint32_t *>(scw + o + j * 32 * 16);
+    };
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); loads stay in flight
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    f32x16_t acc[MTM][MTN];
+#pragma unroll
+    for (int i = 0; i < MTM; ++i)
+#pragma unroll
+        for (int j = 0; j < MTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    uint4 fa[2][MTM], fb[2][MTN];
+    uint32_t sa[2][MTM], sw[2][MTN];
+    MxRegs R0, R1;  // named (not an array), so they stay in registers
+    u32x4_t RS;     // the next scale group
+
+    // Every step loads codes two steps ahead (past the end, a repeat of the
+    // last step) and stores one step, so the steps are straight-line code;
+    // the third step of a group loads the next group's scales, the fourth
+    // stores them.
+    load_regs(R0, 0);
+    store_regs(R0, 0);
+    store_scales(load_scales(0), 0);
+    load_regs(R1, min(1, KT - 1));
+    lds_barrier();
+    read_frags(0, 0, fa[0], fb[0]);
+    read_scales(0, sa[0], sw[0]);
+
+    // step kt = 4 j + u on code stage b = u % 2 (constants in each unrolled copy)
+    auto step = [&](int kt, auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value, b = u & 1;
+        uint32_t ssa[MTM], ssw[MTN];
+#pragma unroll
+        for (int i = 0; i < MTM; ++i) ssa[i] = sa[b][i] >> sh;
+#pragma unroll
+        for (int j = 0; j < MTN; ++j) ssw[j] = sw[b][j] >> sh;
+        // R0 / R1 alternate: the free one loads step kt + 2, the other holds kt + 1
+        if constexpr (b == 0)
+            load_regs(R0, min(kt + 2, KT - 1));
+        else
+            load_regs(R1, min(kt + 2, KT - 1));
+        if constexpr (u == 2) RS = load_scales(min((kt >> 2) + 1, (KT >> 2) - 1));
+        read_frags(b, 1, fa[1], fb[1]);
+        // the schedule is kept as written: reads ahead of the MFMAs that
+        // cover them, nothing moved across the phases (registers)
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfmas(acc, fa[0], fb[0], ssa, ssw, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (b == 0)
+            store_regs(R1, 1);
+        else
+            store_regs(R0, 0);
+        if constexpr (u == 3) store_scales(RS, ((kt >> 2) + 1) & 1);
+        lds_barrier();
+        // (after the last step these read stages nobody uses)
+        read_frags(b ^ 1, 0, fa[0], fb[0]);
+        read_scales(kt + 1, sa[b ^ 1], sw[b ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfmas(acc, fa[1], fb[1], ssa, ssw, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < KT; kt += 4) {
+        step(kt, std::integral_constant<int, 0>());
+        step(kt + 1, std::integral_constant<int, 1>());
+        step(kt + 2, std::integral_constant<int, 2>());
+        step(kt + 3, std::integral_constant<int, 3>());
+    }
+    mx_store<kOutBf16>(g, acc, m0, n0);
+}
+
+// Edge tiles and K % 512 != 0: K step 256, two LDS stages staged through
+// registers; rows past M/N repeat the last row, code chunks past K are zero
+// and their scales 1.0 (code 127).
 __device__ __forceinline__ void stage_guarded(const MxArgs &g, uint8_t *stage, int64_t m0, int64_t n0, int kt) {
     const int64_t rb = g.K >> 1, sb = g.K >> 5;
 #pragma unroll
@@ -177,22 +355,11 @@ __device__ __forceinline__ void stage_guarded(const MxArgs &g, uint8_t *stage, i
 }
 
 template <bool kOutBf16>
-__global__ __launch_bounds__(MNT, 1) void mx_gemm_kernel(MxArgs g) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    int tm, tn;
-    tile_coords<MBM, MBN>(g.M, g.N, tm, tn);
-    const int64_t m0 = (int64_t)tm * MBM, n0 = (int64_t)tn * MBN;
+__device__ __forceinline__ void mx_tile_staged(const MxArgs &g, uint8_t *smem, int64_t m0, int64_t n0) {
     const int KT = (int)((g.K + 255) / 256);
-    const bool direct = m0 + MBM <= g.M && n0 + MBN <= g.N && (g.K & 255) == 0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / MWGN, wn = wave % MWGN;
     auto stage = [&](int s) { return smem + s * STAGE; };
-    auto fill = [&](int s, int kt) __attribute__((always_inline)) {
-        if (direct)
-            stage_direct(g, stage(s), m0, n0, kt);
-        else
-            stage_guarded(g, stage(s), m0, n0, kt);
-    };
 
     f32x16_t acc[MTM][MTN];
 #pragma unroll
@@ -202,12 +369,11 @@ __global__ __launch_bounds__(MNT, 1) void mx_gemm_kernel(MxArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (KT > 0) fill(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (KT > 0) stage_guarded(g, stage(0), m0, n0, 0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) fill(cur ^ 1, kt + 1);
+        if (kt + 1 < KT) stage_guarded(g, stage(cur ^ 1), m0, n0, kt + 1);
         const uint8_t *A = stage(cur), *W = stage(cur) + CODE_TILE;
         const uint8_t *SA = stage(cur) + 2 * CODE_TILE, *SW = SA + SCALE_TILE;
         // per fragment row: the step's 8 E8M0 scales, shifted so that byte
@@ -239,45 +405,28 @@ __global__ __launch_bounds__(MNT, 1) void mx_gemm_kernel(MxArgs g) {
 #pragma unroll
         for (int ks = 0; ks < MKS; ++ks) {
             if (ks + 1 < MKS) read_frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            uint32_t sai[MTM], swj[MTN];
 #pragma unroll
-            for (int i = 0; i < MTM; ++i) {
-                const uint4 a = af[ks & 1][i];
-                const i32x8_t a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-                const int sai = (int)((ks >> 1) ? sa[i].y : sa[i].x);
+            for (int i = 0; i < MTM; ++i) sai[i] = (ks >> 1) ? sa[i].y : sa[i].x;
 #pragma unroll
-                for (int j = 0; j < MTN; ++j) {
-                    const uint4 b = bf[ks & 1][j];
-                    const i32x8_t b8 = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-                    const int swj = (int)((ks >> 1) ? sw[j].y : sw[j].x);
-                    if (ks & 1)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 2, sai,
-                                                                                    2, swj);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0, sai,
-                                                                                    0, swj);
-                }
-            }
+            for (int j = 0; j < MTN; ++j) swj[j] = (ks >> 1) ? sw[j].y : sw[j].x;
+            mx_mfmas(acc, af[ks & 1], bf[ks & 1], sai, swj, ks & 1);
         }
-        __builtin_amdgcn_s_waitcnt(0);  // the next stage (direct loads) has landed
         __syncthreads();
     }
+    mx_store<kOutBf16>(g, acc, m0, n0);
+}
 
-#pragma unroll
-    for (int i = 0; i < MTM; ++i)
-#pragma unroll
-        for (int j = 0; j < MTN; ++j) {
-            const int64_t col = n0 + wn * MWN + j * 32 + (lane & 31);
-            if (col >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * MWM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row >= g.M) continue;
-                if (kOutBf16)
-                    reinterpret_cast<__bf16 *>(g.out)[row * g.ld_out + col] = (__bf16)acc[i][j][r];
-                else
-                    reinterpret_cast<float *>(g.out)[row * g.ld_out + col] = acc[i][j][r];
-            }
-        }
+template <bool kOutBf16>
+__global__ __launch_bounds__(MNT, 1) void mx_gemm_kernel(MxArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int tm, tn;
+    tile_coords<MBM, MBN>(g.M, g.N, tm, tn);
+    const int64_t m0 = (int64_t)tm * MBM, n0 = (int64_t)tn * MBN;
+    if (m0 + MBM <= g.M && n0 + MBN <= g.N && (g.K & 511) == 0)
+        mx_tile_pipe<kOutBf16>(g, smem, m0, n0);
+    else
+        mx_tile_staged<kOutBf16>(g, smem, m0, n0);
 }
 
 template <bool kOutBf16>

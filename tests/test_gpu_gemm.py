@@ -70,7 +70,10 @@ def test_tiny_config_full(nv, oracle_mod):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (1, 300, 48), (127, 129, 80), (130, 257, 272), (300, 520, 1024),
-                                   (64, 64, 4096), (256, 128, 16)])
+                                   (64, 64, 4096), (256, 128, 16),
+                                   # interior tiles with K % 256 == 0 fetch block scales per group of
+                                   # four K steps: one, two and three groups, and mixed with edge tiles
+                                   (256, 256, 256), (384, 256, 512), (128, 128, 768), (300, 520, 768)])
 def test_ragged_shapes(nv, oracle_mod, M, N, K):
     g = np.random.default_rng(M * 7 + N * 13 + K)
     a = wl.to_bf16_bits(g.standard_normal((M, K), dtype=np.float32))

@@ -96,7 +96,13 @@ def test_gemm_unit_scales(nv, oracle_mod, M, N, K):
     _check(nv, A, W, oracle_mod.mx_gemm(*A, *W), f"unit scales {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 300, 96), (130, 257, 288), (256, 512, 4096), (300, 520, 1056)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 300, 96), (130, 257, 288), (256, 512, 4096), (300, 520, 1056),
+                                   # K % 512 != 0: every tile on the register-staged K-256 path
+                                   (256, 256, 128), (256, 512, 384), (512, 256, 640), (256, 256, 896),
+                                   # interior tiles with K % 512 == 0 take the pipelined path (1, 2, 3 and
+                                   # 5 scale groups); the last case mixes it with edge tiles in one launch
+                                   (256, 256, 512), (256, 512, 1024), (512, 256, 1536), (512, 768, 2560),
+                                   (300, 520, 1536)])
 def test_gemm_random_scales(nv, oracle_mod, M, N, K):
     g = np.random.default_rng(M * 3 + N + K)
     A = (g.integers(0, 256, size=(M, K // 2), dtype=np.uint8), g.integers(110, 140, size=(M, K // 32)).astype(np.uint8))
