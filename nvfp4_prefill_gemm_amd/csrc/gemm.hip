@@ -194,40 +194,48 @@ struct Bf16Stage {
     u32x4_t v[EPT / 8];
 };
 
+
+// BF16 operands (BF16 kind, and A of the fused kind), row-interleaved: load c
+// of thread t is 16-byte chunk (t + NT c) % 8 of tile row (t + NT c) / 8, so
+// each wave instruction reads 8 whole 128-byte row segments (8 L2 requests);
+// a thread per row read one 16-byte piece of 64 rows per instruction (64
+// requests), 5% slower for the BF16 GEMM at 8192 tokens, 12% at 512.
 template <int R, int NT, int kMode>
-__device__ __forceinline__ void bf16_load(Bf16Stage<Part<R, NT>::EPT> &st, const uint16_t *__restrict__ x, int64_t ld,
-                                          int64_t rows, int64_t K, int64_t row0, int kt) {
+__device__ __forceinline__ void bf16_load(Bf16Stage<Part<R, NT>::EPT> &st, const uint16_t *__restrict__ x,
+                                             int64_t ld, int64_t rows, int64_t K, int64_t row0, int kt) {
     constexpr int EPT = Part<R, NT>::EPT;
-    const int64_t row = row0 + Part<R, NT>::row();
-    const int64_t k0 = (int64_t)kt * BK + Part<R, NT>::part() * EPT;
+    static_assert(BK == 64, "8 chunks per row and step");
     if (kMode <= 1) {  // buffer resource over the valid rows (see fp4_load)
         const int64_t nrows = rows - row0 < R ? rows - row0 : R;
         const rsrc_t xs = make_rsrc(x + row0 * ld, (uint32_t)(nrows * ld * 2));
-        const uint32_t xo = ((uint32_t)Part<R, NT>::row() * (uint32_t)ld + (uint32_t)k0) * 2u;
 #pragma unroll
-        for (int c = 0; c < EPT / 8; ++c) st.v[c] = __builtin_bit_cast(u32x4_t, buf_load16(xs, xo + 16 * c));
+        for (int c = 0; c < EPT / 8; ++c) {
+            const uint32_t id = threadIdx.x + NT * c;
+            const uint32_t xo = ((id >> 3) * (uint32_t)ld + (uint32_t)kt * BK + (id & 7) * 8) * 2u;
+            st.v[c] = __builtin_bit_cast(u32x4_t, buf_load16(xs, xo));
+        }
         return;
     }
-    if (kMode == 3) {  // interior tile, K % 64 == 0
 #pragma unroll
-        for (int c = 0; c < EPT / 8; ++c) st.v[c] = *reinterpret_cast<const u32x4_t *>(x + row * ld + k0 + 8 * c);
-        return;
+    for (int c = 0; c < EPT / 8; ++c) {
+        const int id = threadIdx.x + NT * c;
+        const int64_t row = row0 + (id >> 3), k = (int64_t)kt * BK + (id & 7) * 8;
+        st.v[c] = (kMode == 3 || (row < rows && k + 8 <= K)) ? *reinterpret_cast<const u32x4_t *>(x + row * ld + k)
+                                                            : u32x4_t{0, 0, 0, 0};
     }
-    const bool rin = row < rows;
-    const uint16_t *p = x + (rin ? row : 0) * ld + k0;
-#pragma unroll
-    for (int c = 0; c < EPT / 8; ++c)
-        st.v[c] = (rin && k0 + 8 * c + 8 <= K) ? *reinterpret_cast<const u32x4_t *>(p + 8 * c) : u32x4_t{0, 0, 0, 0};
 }
 
 template <int R, int NT, int H = -1>
 __device__ __forceinline__ void bf16_store(const Bf16Stage<Part<R, NT>::EPT> &st, uint16_t *lds) {
     constexpr int EPT = Part<R, NT>::EPT;
     constexpr int NC = EPT / 8, C0 = H < 0 ? 0 : H * NC / 2, C1 = H < 0 ? NC : (H + 1) * NC / 2;
-    const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
 #pragma unroll
-    for (int c = C0; c < C1; ++c) *reinterpret_cast<u32x4_t *>(lds + lds_off(r, c0 + c)) = st.v[c];
+    for (int c = C0; c < C1; ++c) {
+        const int id = threadIdx.x + NT * c;
+        *reinterpret_cast<u32x4_t *>(lds + lds_off(id >> 3, id & 7)) = st.v[c];
+    }
 }
+
 
 // Per-workgroup constants of the fused prologue: the tensor scale, Eq. 3's
 // t = alpha * 6 with rt = RN(1/t) and the range where the corrected quotient
@@ -240,25 +248,31 @@ struct FusedQuant {
     const float4 *dtab;
 };
 
+
 // Fused prologue: quantize the staged BF16 values with the standalone
 // quantizer's arithmetic (Eq. 3 by the corrected quotient against t, else the
 // IEEE quotient; Eq. 2 by quant8_fast, or quant8 for a block outside its
-// range), then expand q * sigma.
+// range), then expand q * sigma.  A lane holds half a block (8 elements, the
+// row-interleaved staging above); the block amax takes the partner lane's
+// half by one DPP swap, both lanes form the block's scale, and each
+// quantizes its own 8 elements.
 template <int R, int NT, int H = -1>
-__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds, const FusedQuant &fq) {
+__device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &st, half_t *lds,
+                                               const FusedQuant &fq) {
     constexpr int EPT = Part<R, NT>::EPT;
-    constexpr int NB = EPT / 16, B0 = H < 0 ? 0 : H * NB / 2, B1 = H < 0 ? NB : (H + 1) * NB / 2;
-    const int r = Part<R, NT>::row(), c0 = Part<R, NT>::part() * (EPT / 8);
+    constexpr int NC = EPT / 8, C0 = H < 0 ? 0 : H * NC / 2, C1 = H < 0 ? NC : (H + 1) * NC / 2;
 #pragma unroll
-    for (int b = B0; b < B1; ++b) {
-        const uint32_t w[8] = {st.v[2 * b].x, st.v[2 * b].y, st.v[2 * b].z, st.v[2 * b].w,
-                               st.v[2 * b + 1].x, st.v[2 * b + 1].y, st.v[2 * b + 1].z, st.v[2 * b + 1].w};
-        // block amax over the elements as FP32 (the values quant8_fast forms)
-        float amax_b = 0.0f;
+    for (int c = C0; c < C1; ++c) {
+        const int id = threadIdx.x + NT * c;
+        const uint32_t w[4] = {st.v[c].x, st.v[c].y, st.v[c].z, st.v[c].w};
+        float am = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            amax_b = __builtin_fmaxf(amax_b, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w[i] << 16)),
-                                                             __builtin_fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+        for (int i = 0; i < 4; ++i)
+            am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w[i] << 16)),
+                                                     __builtin_fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+        const float amax_b =  // the block's other half sits in lane ^ 1
+            __builtin_fmaxf(am, __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(am), 0xB1,
+                                                                                  0xF, 0xF, false)));
         float sq = 0.0f;  // Eq. 3
         if (fq.t > 0.0f) {
             const float q0 = amax_b * fq.rt;
@@ -268,12 +282,8 @@ __device__ __forceinline__ void fused_store(const Bf16Stage<Part<R, NT>::EPT> &s
         }
         const uint32_t code = e4m3_encode(sq);
         const float4 e = fq.dtab[code];
-        const half2_t s2 = e4m3_to_f16x2_over256(code);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint32_t packed = amax_b <= e.z ? quant8_fast(&w[4 * c], e.x, e.y) : quant8(&w[4 * c], e.x);
-            *reinterpret_cast<half8_t *>(lds + lds_off(r, c0 + 2 * b + c)) = expand8(packed, s2);
-        }
+        const uint32_t packed = amax_b <= e.z ? quant8_fast(w, e.x, e.y) : quant8(w, e.x);
+        *reinterpret_cast<half8_t *>(lds + lds_off(id >> 3, id & 7)) = expand8(packed, e4m3_to_f16x2_over256(code));
     }
 }
 
