@@ -210,6 +210,69 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     }
     const uint8_t *lc = nullptr, *ls = nullptr;  // LDS copy of A (fused path)
     float alpha_a = 0.0f;
+    // Two register stages of U chunks each, as in the BF16 decode kernel.
+    struct NStage {
+        uint4 wq[U][NG], xq[U][MG];
+        uint32_t wsc[U][NG], xsc[U][MG];
+    };
+    // weights (w) and the batch (x) of a stage; the fused path issues the
+    // first stage's weight loads before it quantizes the batch
+    auto load_part = [&](int64_t c0, NStage &st, bool do_w, bool do_x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = (c0 + (int64_t)u * WAVES) * 128 + kg;
+            const bool kin = k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
+            const uint32_t kc = (uint32_t)(k >> 1), ksc = (uint32_t)(k >> 4);
+            if (do_w) {
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + kc : kBufOOB);
+                    st.wsc[u][j] = buf_load2(wss, kin ? wso[j] + ksc : kBufOOB);
+                }
+            }
+            if (!do_x) continue;
+#pragma unroll
+            for (int i = 0; i < MG; ++i) {
+                if constexpr (kA == A_NVFP4) {
+                    st.xq[u][i] = buf_load16(xcs, (kin & xv[i]) ? xco[i] + kc : kBufOOB);
+                    st.xsc[u][i] = buf_load2(xss, (kin & xv[i]) ? xso[i] + ksc : kBufOOB);
+                } else {  // LDS: clamp the address, zero by select
+                    const uint32_t kk = kin ? kc : 0u, kks = kin ? ksc : 0u;
+                    const uint4 q = *reinterpret_cast<const uint4 *>(lc + xco[i] + kk);
+                    const uint32_t sc = *reinterpret_cast<const uint16_t *>(ls + xso[i] + kks);
+                    st.xq[u][i] = (kin & xv[i]) ? q : make_uint4(0, 0, 0, 0);
+                    st.xsc[u][i] = (kin & xv[i]) ? sc : 0u;
+                }
+            }
+        }
+    };
+    auto load = [&](int64_t c0, NStage &st) __attribute__((always_inline)) { load_part(c0, st, true, true); };
+    auto compute = [&](const NStage &st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                half8_t b[NG];
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    const uint4 q = st.wq[u][j];
+                    const uint32_t w = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
+                    b[j] = expand8(w, e4m3_to_f16x2_over256(t < 2 ? (st.wsc[u][j] & 0xFFu) : (st.wsc[u][j] >> 8)));
+                }
+#pragma unroll
+                for (int i = 0; i < MG; ++i) {
+                    const uint4 q = st.xq[u][i];
+                    const uint32_t xw = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
+                    const half8_t a =
+                        expand8(xw, e4m3_to_f16x2_over256(t < 2 ? (st.xsc[u][i] & 0xFFu) : (st.xsc[u][i] >> 8)));
+#pragma unroll
+                    for (int j = 0; j < NG; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+                }
+            }
+    };
+    NStage s0, s1;
+    if constexpr (kA != A_NVFP4) load_part(wave, s0, true, false);
     if constexpr (kA != A_NVFP4) {
         // quantize the whole batch into LDS: codes [M][K/2], then scales [M][K/16]
         extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
@@ -269,65 +332,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         ls = lsw;
     }
 
-    // Two register stages of U chunks each, as in the BF16 decode kernel.
-    struct NStage {
-        uint4 wq[U][NG], xq[U][MG];
-        uint32_t wsc[U][NG], xsc[U][MG];
-    };
-    auto load = [&](int64_t c0, NStage &st) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = (c0 + (int64_t)u * WAVES) * 128 + kg;
-            const bool kin = k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
-            const uint32_t kc = (uint32_t)(k >> 1), ksc = (uint32_t)(k >> 4);
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + kc : kBufOOB);
-                st.wsc[u][j] = buf_load2(wss, kin ? wso[j] + ksc : kBufOOB);
-            }
-#pragma unroll
-            for (int i = 0; i < MG; ++i) {
-                if constexpr (kA == A_NVFP4) {
-                    st.xq[u][i] = buf_load16(xcs, (kin & xv[i]) ? xco[i] + kc : kBufOOB);
-                    st.xsc[u][i] = buf_load2(xss, (kin & xv[i]) ? xso[i] + ksc : kBufOOB);
-                } else {  // LDS: clamp the address, zero by select
-                    const uint32_t kk = kin ? kc : 0u, kks = kin ? ksc : 0u;
-                    const uint4 q = *reinterpret_cast<const uint4 *>(lc + xco[i] + kk);
-                    const uint32_t sc = *reinterpret_cast<const uint16_t *>(ls + xso[i] + kks);
-                    st.xq[u][i] = (kin & xv[i]) ? q : make_uint4(0, 0, 0, 0);
-                    st.xsc[u][i] = (kin & xv[i]) ? sc : 0u;
-                }
-            }
-        }
-    };
-    auto compute = [&](const NStage &st) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                half8_t b[NG];
-#pragma unroll
-                for (int j = 0; j < NG; ++j) {
-                    const uint4 q = st.wq[u][j];
-                    const uint32_t w = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
-                    b[j] = expand8(w, e4m3_to_f16x2_over256(t < 2 ? (st.wsc[u][j] & 0xFFu) : (st.wsc[u][j] >> 8)));
-                }
-#pragma unroll
-                for (int i = 0; i < MG; ++i) {
-                    const uint4 q = st.xq[u][i];
-                    const uint32_t xw = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
-                    const half8_t a =
-                        expand8(xw, e4m3_to_f16x2_over256(t < 2 ? (st.xsc[u][i] & 0xFFu) : (st.xsc[u][i] >> 8)));
-#pragma unroll
-                    for (int j = 0; j < NG; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
-                }
-            }
-    };
     const int64_t stride = (int64_t)WAVES * U;
-    NStage s0, s1;
     int64_t c0 = wave;
-    load(c0, s0);
+    if constexpr (kA != A_NVFP4) load_part(c0, s0, false, true);  // the weights are in flight already
+    else load(c0, s0);
     for (;;) {
         const int64_t c1 = c0 + stride;
         load(c1, s1);
@@ -468,9 +476,25 @@ hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, 
                                const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K,
                                void *out, int out_type, int64_t ld_out, hipStream_t s) {
     if (M > 16 || M * K > kFusedDecodeMaxElems) return hipErrorInvalidValue;
-    if (dynamic)
+    // wide layers: several 16-row weight groups per workgroup, so fewer
+    // workgroups quantize the batch (every one of them does)
+    const int ng = N >= 16384 ? 4 : N >= 6144 ? 2 : 1;
+    if (dynamic) {
+        if (ng == 4)
+            return launch_nvfp4_cfg<1, 4, 8, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha,
+                                                                M, N, K, out, out_type, ld_out, s, x, ld_x);
+        if (ng == 2)
+            return launch_nvfp4_cfg<1, 2, 8, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha,
+                                                                M, N, K, out, out_type, ld_out, s, x, ld_x);
         return launch_nvfp4_cfg<1, 1, 16, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M,
                                                              N, K, out, out_type, ld_out, s, x, ld_x);
+    }
+    if (ng == 4)
+        return launch_nvfp4_cfg<1, 4, 8, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
+                                                           K, out, out_type, ld_out, s, x, ld_x);
+    if (ng == 2)
+        return launch_nvfp4_cfg<1, 2, 8, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
+                                                           K, out, out_type, ld_out, s, x, ld_x);
     return launch_nvfp4_cfg<1, 1, 16, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
                                                         K, out, out_type, ld_out, s, x, ld_x);
 }

@@ -113,7 +113,9 @@ def test_decode_kernel_agrees_with_tile_kernel(nv, oracle_mod):
 
 @pytest.mark.parametrize("M,N,K,ld_pad", [(1, 6144, 4096, 0), (1, 4096, 12288, 0), (2, 300, 4128, 8),
                                           (8, 24576, 4096, 0), (13, 17, 96, 24), (16, 1000, 1056, 0),
-                                          (16, 64, 12288, 0), (1, 520, 65536, 0)])
+                                          (16, 64, 12288, 0), (1, 520, 65536, 0),
+                                          # two and four 16-row weight groups per workgroup, last one partial
+                                          (3, 6200, 1056, 0), (1, 16400, 512, 8)])
 def test_fused_decode_equals_quantize_then_gemm(nv, oracle_mod, M, N, K, ld_pad):
     """nvfp4_quant_gemm with M <= 16 and M * K <= 196608 quantizes the batch
     inside the decode kernel: alpha, and the output in FP32 and BF16, equal
