@@ -450,7 +450,10 @@ hipError_t launch_nv_ng(const uint8_t *ac, const uint8_t *as, const float *aa_in
                         int64_t ld_out, hipStream_t s) {
     float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
     int ng = decode_ng_knob();
-    if (ng == 0) ng = MG == 4 && N >= 6144 ? 2 : 1;
+    // two 16-row weight groups per workgroup on wide layers (each X fragment
+    // then serves both): measured faster from N = 6144 at one and four row
+    // groups, slower at N = 4096; four groups were slower everywhere
+    if (ng == 0) ng = (MG == 1 || MG == 4) && N >= 6144 ? 2 : 1;
     if (MG == 4 && ng == 4) ng = 2;  // four row groups by four column groups exceed the register file
     constexpr int U = MG == 1 ? 2 : 1;  // chunks per register stage
     switch (ng) {

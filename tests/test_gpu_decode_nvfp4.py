@@ -70,7 +70,9 @@ def _random_operand(g, rows, K, lo=0, hi=127):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 15, 96), (16, 17, 160), (17, 300, 4128), (33, 64, 288),
-                                   (64, 1000, 1056), (63, 31, 12288)])
+                                   (64, 1000, 1056), (63, 31, 12288),
+                                   # wide layers: two 16-row weight groups per workgroup, the last partial
+                                   (5, 6200, 1056), (60, 6170, 288)])
 def test_decode_nvfp4_ragged(nv, oracle_mod, M, N, K):
     """Ragged M/N/K (K not a multiple of the 128-wide chunk, N not a multiple
     of 16, M in every row-group count), random codes and scale codes
