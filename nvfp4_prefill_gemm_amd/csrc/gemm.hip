@@ -18,10 +18,9 @@
 // 512-thread workgroup, 2 x 4 waves of 128 x 64 (a 4 x 2 grid of 32x32x16
 // MFMAs each, 128 FP32 accumulators per lane; two waves per SIMD, so one
 // wave's staging work overlaps the other's MFMAs), K step 64 and a double-
-// buffered LDS stage of 2 x 64 KB; the NVFP4-output epilogue and the fused
-// prologue a 256 x 256 tile of 4 waves of 128 x 128 (their registers do not
-// fit beside 8 waves); small problems a 128 x 128 tile of 4 waves of
-// 64 x 64.  Operand fragments are read from LDS one k16 step ahead
+// buffered LDS stage of 2 x 64 KB; the fused prologue a 256 x 256 tile of
+// 4 waves of 128 x 128 (its registers do not fit beside 8 waves); small
+// problems a 128 x 128 tile of 4 waves of 64 x 64.  Operand fragments are read from LDS one k16 step ahead
 // of the MFMAs that use them; the next K step's global loads are issued
 // before the current step's MFMAs (through buffer resources: see the
 // loaders).  LDS rows are 64 halves = eight 16-byte
@@ -726,7 +725,7 @@ int tile_override() {
 
 template <class C, int kKind>
 hipError_t launch_out(const GemmArgs &g, int out_type, hipStream_t s) {
-    if constexpr (kKind == KIND_NVFP4 && C::NT != 512)
+    if constexpr (kKind == KIND_NVFP4)
         if (out_type == OUT_NVFP4) return launch_cfg<C, kKind, OUT_NVFP4>(g, s);
     if (out_type == OUT_NVFP4) return hipErrorInvalidValue;
     return out_type == OUT_BF16 ? launch_cfg<C, kKind, OUT_BF16>(g, s) : launch_cfg<C, kKind, OUT_F32>(g, s);
@@ -736,12 +735,10 @@ template <int kKind>
 hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
     int t = tile_override();
     if (t == 0) t = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256 ? 2 : 3;
-    // the quantizing epilogue and the fused prologue need more registers
-    // than 8 waves leave the main loop (they spill there): the 4-wave
-    // 256 x 256 tile (512 registers per lane) runs them
-    // (the NVFP4-output epilogue is not built for 8 waves; the fused kind
-    // still takes an explicit NVFP4_GEMM_TILE=big8)
-    if (t == 2 && (out_type == OUT_NVFP4 || (kKind == KIND_FUSED && tile_override() == 0))) t = 1;
+    // the fused prologue needs more registers than 8 waves leave the main
+    // loop (it spills there): the 4-wave 256 x 256 tile (512 registers per
+    // lane) runs it (an explicit NVFP4_GEMM_TILE=big8 still takes 8 waves)
+    if (t == 2 && kKind == KIND_FUSED && tile_override() == 0) t = 1;
     if (t == 1) return launch_out<BigTile, kKind>(g, out_type, s);
     if (t == 2) return launch_out<BigTile8, kKind>(g, out_type, s);
     return launch_out<SmallTile, kKind>(g, out_type, s);
