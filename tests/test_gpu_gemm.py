@@ -122,6 +122,39 @@ def test_k_zero_and_empty(nv):
     assert tuple(out.shape) == (0, 4)
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (4096, 4096, 512)])
+def test_scales_four_byte_aligned(nv, oracle_mod, M, N, K):
+    """Scale arrays at the documented minimum alignment (4 bytes, not 8):
+    interior tiles with K % 256 == 0 fetch a row's block scales 8 bytes at a
+    time, so these loads are 4-byte aligned here.  The 128 x 128 tile and the
+    8-wave 256 x 256 tile; same result as 16-byte aligned scales, and the
+    oracle on sampled outputs."""
+    import torch
+
+    g = np.random.default_rng(M + 3 * K)
+    qa = g.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    qw = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sa = g.integers(0, 127, size=(M, K // 16)).astype(np.uint8)
+    sw = g.integers(0, 127, size=(N, K // 16)).astype(np.uint8)
+    one = f32_dev([1.0])
+
+    def off4(a):
+        buf = torch.zeros(a.size + 4, dtype=torch.uint8, device="cuda")
+        v = buf[4:].view(a.shape)
+        v.copy_(torch.from_numpy(a).cuda())
+        assert v.data_ptr() % 8 == 4
+        return v
+
+    say("nvfp4 gemm 4-byte aligned scales", M, N, K)
+    y_al = nv.nvfp4_gemm(u8_dev(qa), u8_dev(sa), one, u8_dev(qw), u8_dev(sw), one, out_dtype=torch.float32)
+    y_off = nv.nvfp4_gemm(u8_dev(qa), off4(sa), one, u8_dev(qw), off4(sw), one, out_dtype=torch.float32)
+    assert torch.equal(y_off, y_al), "4-byte aligned scales change the result"
+    mi, ni = _sample_pairs(M, N, 2000, M + K)
+    ref = oracle_mod.gemm_exact_pairs(qa, sa, np.float32(1.0), qw, sw, np.float32(1.0), mi, ni)
+    got = y_off[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy().astype(np.float64)
+    parity.assert_gemm_close(got, ref, parity.GEMM_TOL_F32, f"4-byte aligned scales {M}x{N}x{K}")
+
+
 def _sample_pairs(M, N, n, seed):
     g = np.random.default_rng(seed)
     mi = np.concatenate([g.integers(0, M, n), [0, M - 1, M - 1, 0]])
