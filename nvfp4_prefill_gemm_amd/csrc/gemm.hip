@@ -702,12 +702,8 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     GemmArgs ga = g;
     const int64_t a_row = kKind == KIND_NVFP4 ? g.K / 2 : g.lda * 2, w_row = kKind == KIND_BF16 ? g.K * 2 : g.K / 2;
     ga.rows_rsrc = C::BM * a_row < (int64_t(1) << 31) && C::BN * w_row < (int64_t(1) << 31);
-    static bool attr_set = false;  // benign race: setting it twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> attr_done{0};
+    if (hipError_t e = set_dyn_lds_once(attr_done, (const void *)kern, (int)lds_bytes); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds_bytes, s, ga);
     return hipGetLastError();
 }

@@ -4,7 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
+
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device and process (`done` holds one bit per device id below 32;
+// devices beyond that set it on every call).  The attribute is per device, so
+// a process that drives several GPUs sets it on each.
+inline hipError_t set_dyn_lds_once(std::atomic<uint32_t> &done, const void *kern, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint32_t bit = dev >= 0 && dev < 32 ? 1u << dev : 0u;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
 
 // Number of per-workgroup partial maxima the amax pass writes for a tensor.
 int amax_parts(int64_t rows, int64_t cols);

@@ -435,13 +435,9 @@ hipError_t launch_mx(const MxArgs &g, hipStream_t s) {
     if (nb <= 0) return hipSuccess;
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     const size_t lds = 2 * (size_t)STAGE;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mx_gemm_kernel<kOutBf16>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::atomic<uint32_t> attr_done{0};
+    if (hipError_t e = set_dyn_lds_once(attr_done, (const void *)mx_gemm_kernel<kOutBf16>, (int)lds); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(mx_gemm_kernel<kOutBf16>, dim3((unsigned)nb), dim3(MNT), lds, s, g);
     return hipGetLastError();
 }

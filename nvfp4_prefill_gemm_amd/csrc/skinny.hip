@@ -359,16 +359,12 @@ hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, con
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     const size_t lds = kA == A_NVFP4 ? 0 : (size_t)(M * K / 2 + M * K / 16);
     if (kA != A_NVFP4) {
-        static bool attr[2] = {false, false};
+        static std::atomic<uint32_t> attr_done[2];
         const int o = out_type == OUT_BF16;
-        if (!attr[o]) {
-            const void *f = o ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>
-                              : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, false, kA>;
-            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)(kFusedDecodeMaxElems * 9 / 16));
-            if (e != hipSuccess) return e;
-            attr[o] = true;
-        }
+        const void *f = o ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>
+                          : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, false, kA>;
+        if (hipError_t e = set_dyn_lds_once(attr_done[o], f, (int)(kFusedDecodeMaxElems * 9 / 16)); e != hipSuccess)
+            return e;
     }
     if (out_type == OUT_BF16)
         hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>), dim3((unsigned)nb), dim3(WAVES * 64),
