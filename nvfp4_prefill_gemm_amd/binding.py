@@ -79,10 +79,86 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# Argument checks run before any C call: the C ABI sees only pointers and
+# sizes, so a tensor whose shape, dtype, layout or device disagrees with the
+# sizes passed would make the kernels read or write outside it.  Shapes,
+# dtypes and layouts are checked first, devices last.
+
+def _tensor(t, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    return t
+
+
+def _mat(t, name: str, dtype, rows: int | None = None, cols: int | None = None, contiguous: bool = True):
+    """2-D tensor of ``dtype`` with the given shape; row-major (contiguous, or
+    rows of unit element stride when ``contiguous`` is False)."""
+    _tensor(t, name)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if rows is not None and t.shape[0] != rows:
+        raise ValueError(f"{name} must have {rows} rows, got shape {tuple(t.shape)}")
+    if cols is not None and t.shape[1] != cols:
+        raise ValueError(f"{name} must have {cols} columns, got shape {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not contiguous and t.shape[0] > 1 and t.shape[1] > 0 and (t.stride(1) != 1 or t.stride(0) < t.shape[1]):
+        raise ValueError(f"{name} must be row-major with unit column stride")
+    return t
+
+
+def _alpha(t, name: str):
+    _tensor(t, name)
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.numel() < 1:
+        raise ValueError(f"{name} must hold at least one element")
+    return t
+
+
+def _out(t, name: str, rows: int, cols: int):
+    """GEMM output [rows, cols], FP32 or BF16, unit column stride (row stride >= cols)."""
+    _tensor(t, name)
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
+    if rows > 0 and cols > 0 and (t.stride(1) != 1 or (rows > 1 and t.stride(0) < cols)):
+        raise ValueError(f"{name} must be row-major with unit column stride")
+    return t
+
+
+def _k_of_codes(codes: torch.Tensor, name: str, multiple: int = 16) -> int:
+    k = codes.shape[1] * 2
+    if k % multiple:
+        raise ValueError(f"{name}: K = {k} must be a multiple of {multiple}")
+    return k
+
+
+def _same_device(*named):
+    """Every tensor on the GPU, and all on one device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 _OUT = {torch.float32: NVFP4_OUT_F32, torch.bfloat16: NVFP4_OUT_BF16}
@@ -99,10 +175,10 @@ def nvfp4_quantize(x: torch.Tensor, codes: torch.Tensor | None = None, scales: t
 
     static_alpha=True reads the tensor scale from ``alpha``; otherwise it is
     computed from the data and written there."""
-    _dev(x, "x", torch.bfloat16)
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D row-major tensor")
+    _mat(x, "x", torch.bfloat16, contiguous=False)
     rows, cols = x.shape
+    if cols % 16:
+        raise ValueError(f"x: cols = {cols} must be a multiple of 16")
     dev = x.device
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
@@ -112,29 +188,45 @@ def nvfp4_quantize(x: torch.Tensor, codes: torch.Tensor | None = None, scales: t
         if static_alpha:
             raise ValueError("static_alpha needs alpha")
         alpha = torch.empty(1, dtype=torch.float32, device=dev)
-    ws_bytes = 0
-    if not static_alpha:
-        ws_bytes = quantize_workspace_size(rows, cols)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=dev)
+    _mat(codes, "codes", torch.uint8, rows, cols // 2)
+    _mat(scales, "scales", torch.uint8, rows, cols // 16)
+    _alpha(alpha, "alpha")
+    if workspace is not None:
+        _tensor(workspace, "workspace")
+    _same_device(("x", x), ("codes", codes), ("scales", scales), ("alpha", alpha), ("workspace", workspace))
+    if not static_alpha and workspace is None:
+        workspace = torch.empty(max(quantize_workspace_size(rows, cols), 4), dtype=torch.uint8, device=dev)
     rc = lib().nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(codes), _ptr(scales), _ptr(alpha),
                               NVFP4_ALPHA_STATIC if static_alpha else NVFP4_ALPHA_DYNAMIC, _ptr(workspace),
-                              workspace.numel() if workspace is not None else 0, _stream(stream))
+                              _nbytes(workspace), _stream(stream))
     _check("nvfp4_quantize", rc)
     return codes, scales, alpha
+
+
+def _nvfp4_operands(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha):
+    """Check both NVFP4 operands; returns (M, N, K)."""
+    _mat(a_codes, "a_codes", torch.uint8)
+    _mat(w_codes, "w_codes", torch.uint8)
+    K = _k_of_codes(a_codes, "a_codes")
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError(f"A and W disagree on K ({K} vs {w_codes.shape[1] * 2})")
+    M, N = a_codes.shape[0], w_codes.shape[0]
+    _mat(a_scales, "a_scales", torch.uint8, M, K // 16)
+    _mat(w_scales, "w_scales", torch.uint8, N, K // 16)
+    _alpha(a_alpha, "a_alpha")
+    _alpha(w_alpha, "w_alpha")
+    return M, N, K
 
 
 def nvfp4_gemm(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, out: torch.Tensor | None = None,
                out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
     """Y [M, N] = dequant(A) @ dequant(W)^T from NVFP4 operands."""
-    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
-        _dev(t, n, torch.uint8)
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K:
-        raise ValueError("A and W disagree on K")
+    M, N, K = _nvfp4_operands(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _out(out, "out", M, N)
+    _same_device(("a_codes", a_codes), ("a_scales", a_scales), ("a_alpha", a_alpha), ("w_codes", w_codes),
+                 ("w_scales", w_scales), ("w_alpha", w_alpha), ("out", out))
     rc = lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_alpha), _ptr(w_codes), _ptr(w_scales),
                           _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _stream(stream))
     _check("nvfp4_gemm", rc)
@@ -145,17 +237,19 @@ def nvfp4_gemm_quant_out(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha,
                          y_codes: torch.Tensor | None = None, y_scales: torch.Tensor | None = None, stream=None):
     """NVFP4 GEMM with an NVFP4 output (static output scale y_alpha, float32 [1]).
     Returns (y_codes uint8 [M, N/2], y_scales uint8 [M, N/16])."""
-    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
-        _dev(t, n, torch.uint8)
-    _dev(y_alpha, "y_alpha", torch.float32)
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K:
-        raise ValueError("A and W disagree on K")
+    M, N, K = _nvfp4_operands(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha)
+    if N % 16:
+        raise ValueError(f"N = {N} must be a multiple of 16 for an NVFP4 output")
+    _alpha(y_alpha, "y_alpha")
     if y_codes is None:
         y_codes = torch.empty((M, N // 2), dtype=torch.uint8, device=a_codes.device)
     if y_scales is None:
         y_scales = torch.empty((M, N // 16), dtype=torch.uint8, device=a_codes.device)
+    _mat(y_codes, "y_codes", torch.uint8, M, N // 2)
+    _mat(y_scales, "y_scales", torch.uint8, M, N // 16)
+    _same_device(("a_codes", a_codes), ("a_scales", a_scales), ("a_alpha", a_alpha), ("w_codes", w_codes),
+                 ("w_scales", w_scales), ("w_alpha", w_alpha), ("y_alpha", y_alpha), ("y_codes", y_codes),
+                 ("y_scales", y_scales))
     rc = lib().nvfp4_gemm_quant_out(_ptr(a_codes), _ptr(a_scales), _ptr(a_alpha), _ptr(w_codes), _ptr(w_scales),
                                     _ptr(w_alpha), M, N, K, _ptr(y_codes), _ptr(y_scales), _ptr(y_alpha),
                                     _stream(stream))
@@ -171,24 +265,32 @@ def nvfp4_quant_gemm(x: torch.Tensor, w_codes, w_scales, w_alpha, a_alpha: torch
                      static_alpha: bool = False, out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
                      workspace: torch.Tensor | None = None, stream=None):
     """Fused prefill linear: BF16 x quantized to NVFP4 inside the GEMM.  Returns (out, a_alpha)."""
-    _dev(x, "x", torch.bfloat16)
+    _mat(x, "x", torch.bfloat16, contiguous=False)
     M, K = x.shape
+    if K % 16:
+        raise ValueError(f"x: K = {K} must be a multiple of 16")
+    _mat(w_codes, "w_codes", torch.uint8, cols=K // 2)
     N = w_codes.shape[0]
+    _mat(w_scales, "w_scales", torch.uint8, N, K // 16)
+    _alpha(w_alpha, "w_alpha")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _out(out, "out", M, N)
     if a_alpha is None:
         if static_alpha:
             raise ValueError("static_alpha needs a_alpha")
         a_alpha = torch.empty(1, dtype=torch.float32, device=x.device)
-    ws_bytes = 0
-    if not static_alpha:
-        ws_bytes = quant_gemm_workspace_size(M, K)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=x.device)
+    _alpha(a_alpha, "a_alpha")
+    if workspace is not None:
+        _tensor(workspace, "workspace")
+    _same_device(("x", x), ("w_codes", w_codes), ("w_scales", w_scales), ("w_alpha", w_alpha), ("out", out),
+                 ("a_alpha", a_alpha), ("workspace", workspace))
+    if not static_alpha and workspace is None:
+        workspace = torch.empty(max(quant_gemm_workspace_size(M, K), 4), dtype=torch.uint8, device=x.device)
     rc = lib().nvfp4_quant_gemm(_ptr(x), x.stride(0), _ptr(a_alpha),
                                 NVFP4_ALPHA_STATIC if static_alpha else NVFP4_ALPHA_DYNAMIC, _ptr(w_codes),
                                 _ptr(w_scales), _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0),
-                                _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
+                                _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check("nvfp4_quant_gemm", rc)
     return out, a_alpha
 
@@ -196,14 +298,14 @@ def nvfp4_quant_gemm(x: torch.Tensor, w_codes, w_scales, w_alpha, a_alpha: torch
 def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
               stream=None) -> torch.Tensor:
     """Y [M, N] = A [M, K] @ W [N, K]^T in BF16 with FP32 accumulation."""
-    _dev(a, "a", torch.bfloat16)
-    _dev(w, "w", torch.bfloat16)
-    if not (a.is_contiguous() and w.is_contiguous()):
-        raise ValueError("a and w must be contiguous")
+    _mat(a, "a", torch.bfloat16)
     M, K = a.shape
+    _mat(w, "w", torch.bfloat16, cols=K)
     N = w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _out(out, "out", M, N)
+    _same_device(("a", a), ("w", w), ("out", out))
     rc = lib().bf16_gemm(_ptr(a), _ptr(w), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _stream(stream))
     _check("bf16_gemm", rc)
     return out
@@ -212,14 +314,17 @@ def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,
 def mxfp4_quantize(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
                    stream=None):
     """BF16 [rows, cols] -> MXFP4 (codes uint8 [rows, cols/2], E8M0 scales uint8 [rows, cols/32])."""
-    _dev(x, "x", torch.bfloat16)
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D row-major tensor")
+    _mat(x, "x", torch.bfloat16, contiguous=False)
     rows, cols = x.shape
+    if cols % 32:
+        raise ValueError(f"x: cols = {cols} must be a multiple of 32")
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _mat(codes, "codes", torch.uint8, rows, cols // 2)
+    _mat(scales, "scales", torch.uint8, rows, cols // 32)
+    _same_device(("x", x), ("codes", codes), ("scales", scales))
     rc = lib().mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(codes), _ptr(scales), _stream(stream))
     _check("mxfp4_quantize", rc)
     return codes, scales
@@ -228,14 +333,19 @@ def mxfp4_quantize(x: torch.Tensor, codes: torch.Tensor | None = None, scales: t
 def mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
                stream=None) -> torch.Tensor:
     """Y [M, N] = dequant(A) @ dequant(W)^T from MXFP4 operands."""
-    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
-        _dev(t, n, torch.uint8)
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    N = w_codes.shape[0]
+    _mat(a_codes, "a_codes", torch.uint8)
+    _mat(w_codes, "w_codes", torch.uint8)
+    K = _k_of_codes(a_codes, "a_codes", 32)
     if w_codes.shape[1] * 2 != K:
-        raise ValueError("A and W disagree on K")
+        raise ValueError(f"A and W disagree on K ({K} vs {w_codes.shape[1] * 2})")
+    M, N = a_codes.shape[0], w_codes.shape[0]
+    _mat(a_scales, "a_scales", torch.uint8, M, K // 32)
+    _mat(w_scales, "w_scales", torch.uint8, N, K // 32)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _out(out, "out", M, N)
+    _same_device(("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes), ("w_scales", w_scales),
+                 ("out", out))
     rc = lib().mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K, _ptr(out),
                           _OUT[out.dtype], out.stride(0), _stream(stream))
     _check("mxfp4_gemm", rc)

@@ -167,6 +167,7 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
         const size_t need = (size_t)nparts * sizeof(uint32_t);
         if (!workspace || workspace_bytes < need)
             return fail(NVFP4_EWORKSPACE, "%s: dynamic alpha needs %zu workspace bytes", fn, need);
+        if (!aligned(workspace, 4)) return fail(NVFP4_EINVAL, "%s: workspace is misaligned", fn);
     }
     if (M <= nvfp4::kFusedDecodeMaxM && M * K <= nvfp4::kFusedDecodeMaxElems && K % 32 == 0)
         return hip_status(nvfp4::launch_skinny_fused((const uint16_t *)x_bf16, ld_x, a_alpha,

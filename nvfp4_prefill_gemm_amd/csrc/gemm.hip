@@ -710,12 +710,13 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
 
 // Tile choice: NVFP4_GEMM_TILE=big4|big8|small overrides (tuning knob);
 // default: a 256 x 256 tile once there are enough tiles to fill the 256 CUs.
+// The variable is read once per process (a function-local static: its
+// initialisation is thread-safe).
 int tile_override() {
-    static int v = -1;
-    if (v < 0) {
+    static const int v = [] {
         const char *e = getenv("NVFP4_GEMM_TILE");
-        v = !e ? 0 : !strcmp(e, "big4") ? 1 : !strcmp(e, "big8") ? 2 : !strcmp(e, "small") ? 3 : 0;
-    }
+        return !e ? 0 : !strcmp(e, "big4") ? 1 : !strcmp(e, "big8") ? 2 : !strcmp(e, "small") ? 3 : 0;
+    }();
     return v;
 }
 

@@ -118,6 +118,7 @@ constexpr int PCODE = MBM * PKB;           // 16 KB
 constexpr int PW = 2 * PCODE;              // W code stages
 constexpr int PSC = 4 * PCODE;             // scale groups: [2][A 256 x 16 B, W 256 x 16 B]
 constexpr int PSG = 2 * MBM * 16;          // 8 KB per group
+constexpr int64_t kMxPipeMaxK = int64_t(1) << 24;
 static_assert(PSC + 2 * PSG <= 2 * STAGE, "the pipelined stages fit the kernel's LDS");
 
 // 16-byte chunk c (of 4) of row r: slot c ^ ((r / 4) % 4), so the 16 rows a
@@ -423,7 +424,10 @@ __global__ __launch_bounds__(MNT, 1) void mx_gemm_kernel(MxArgs g) {
     int tm, tn;
     tile_coords<MBM, MBN>(g.M, g.N, tm, tn);
     const int64_t m0 = (int64_t)tm * MBM, n0 = (int64_t)tn * MBN;
-    if (m0 + MBM <= g.M && n0 + MBN <= g.N && (g.K & 511) == 0)
+    // the pipelined loop addresses a tile's 256 rows through one buffer
+    // resource with 32-bit offsets (256 * K / 2 bytes < 2^31: K < 2^24);
+    // longer rows take the staged loop, which indexes in 64 bits
+    if (m0 + MBM <= g.M && n0 + MBN <= g.N && (g.K & 511) == 0 && g.K < kMxPipeMaxK)
         mx_tile_pipe<kOutBf16>(g, smem, m0, n0);
     else
         mx_tile_staged<kOutBf16>(g, smem, m0, n0);

@@ -222,22 +222,26 @@ int64_t quant_items(int64_t rows, int64_t cols) { return rows * (((cols >> 3) + 
 // Workgroups of the quantize kernel: one per 4 items, at most as many as the
 // device holds at once (each wave then loops over items with its loads
 // pipelined).
+// The per-device count is cached in an atomic: threads that race on the first
+// call compute the same value and store it, so no lock is needed.
 template <bool kDynamic>
 int quant_grid(int64_t rows, int64_t cols) {
-    static int resident[16] = {0};
+    static std::atomic<int> resident_cache[16];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-    if (resident[dev] == 0) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int resident = dev < 16 ? resident_cache[dev].load(std::memory_order_relaxed) : 0;
+    if (resident == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_kernel<kDynamic>, kThreads, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 4;
-        resident[dev] = cus * per_cu;
+        resident = cus * per_cu;
+        if (dev < 16) resident_cache[dev].store(resident, std::memory_order_relaxed);
     }
     int64_t g = (quant_items(rows, cols) + kWaves - 1) / kWaves;
-    if (g > resident[dev]) g = resident[dev];
+    if (g > resident) g = resident;
     return (int)(g < 1 ? 1 : g);
 }
 

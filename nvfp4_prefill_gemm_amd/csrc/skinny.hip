@@ -385,11 +385,10 @@ __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, 
 // NVFP4_SKINNY_CFG=8|16 overrides the waves per workgroup of the BF16 decode
 // kernel with one column group (tuning knob; default 16).
 int skinny_cfg() {
-    static int v = -1;
-    if (v < 0) {
+    static const int v = [] {  // read once; thread-safe initialisation
         const char *e = getenv("NVFP4_SKINNY_CFG");
-        v = (e && !strcmp(e, "8")) ? 1 : 0;
-    }
+        return (e && !strcmp(e, "8")) ? 1 : 0;
+    }();
     return v;
 }
 
@@ -409,12 +408,11 @@ hipError_t launch_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N,
 // NVFP4_DECODE_NG=1|2|4 forces the number of 16-column groups per
 // workgroup (tuning knob); by default it follows the layer width below.
 int decode_ng_knob() {
-    static int v = -1;
-    if (v < 0) {
+    static const int v = [] {  // read once; thread-safe initialisation
         const char *e = getenv("NVFP4_DECODE_NG");
-        v = e ? atoi(e) : 0;
-        if (v != 1 && v != 2 && v != 4) v = 0;
-    }
+        const int n = e ? atoi(e) : 0;
+        return n == 1 || n == 2 || n == 4 ? n : 0;
+    }();
     return v;
 }
 

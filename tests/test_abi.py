@@ -100,3 +100,6 @@ def test_gemm_argument_errors(L):
     f = L.nvfp4_quant_gemm
     assert f(FAKE, 32, FAKE, 0, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None, 0, None) == -4  # workspace
     assert f(FAKE, 16, FAKE, 1, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL  # ld_x
+    misaligned = ctypes.c_void_p(0x1002)  # dynamic alpha stores uint32 partials in the workspace
+    assert f(FAKE, 32, FAKE, 0, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, misaligned, 4096, None) == NVFP4_EINVAL
+    assert b"workspace is misaligned" in L.nvfp4_last_error()
