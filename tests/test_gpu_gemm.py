@@ -177,10 +177,15 @@ def test_qwen3_8b_m8192_sampled(nv, oracle_mod, layer):
     ac, asc, aal = nv.nvfp4_quantize(x)
     wc, wsc, wal = _dev_operand(W)
     y = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.bfloat16)
+    y32 = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.float32)
     mi, ni = _sample_pairs(w.M, N, 4096, layer)
     ref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
-    got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].float().cpu().numpy()
-    parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, f"{name} sampled")
+    idx = (torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda())
+    got = y[idx].float().cpu().numpy().astype(np.float64)
+    got32 = y32[idx].cpu().numpy().astype(np.float64)
+    parity.assert_gemm_close(got32, ref, parity.GEMM_TOL_F32, f"{name} sampled f32")
+    parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, f"{name} sampled bf16")
+    assert np.array_equal(got, _bf16_rne(got32)), f"{name}: BF16 output is not the rounded FP32 output"
 
 
 def test_fused_equals_unfused_and_oracle(nv, oracle_mod):

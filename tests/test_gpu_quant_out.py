@@ -41,10 +41,14 @@ def _tile_fp32(nv, A, W):
     return host(y)[:M]
 
 
-def _check(nv, oracle_mod, A, W, y_alpha, what, ref=None):
+def _check(nv, oracle_mod, A, W, y_alpha, what, ref=None, pairs=None):
+    """ref: the exact product (full); pairs: (mi, ni, exact values there)."""
     y32 = _tile_fp32(nv, A, W)
     if ref is not None:
         parity.assert_gemm_close(y32, ref, parity.GEMM_TOL_F32, what + " fp32")
+    if pairs is not None:
+        mi, ni, pref = pairs
+        parity.assert_gemm_close(y32[mi, ni], pref, parity.GEMM_TOL_F32, what + " fp32 sampled")
     yc, ys = nv.nvfp4_gemm_quant_out(u8_dev(A[0]), u8_dev(A[1]), f32_dev([A[2]]), u8_dev(W[0]), u8_dev(W[1]),
                                      f32_dev([W[2]]), f32_dev([y_alpha]))
     want_c, want_s, _ = oracle_mod.quantize_f32(y32, alpha=float(y_alpha))
@@ -92,13 +96,15 @@ def test_quant_out_qwen3_8b_o_proj_full(nv, oracle_mod):
     A = (host(ac), host(asc), host(aal)[0])
     W = oracle_mod.quantize(wt)
     y_alpha = np.float32(0.02)
-    _check(nv, oracle_mod, A, W, y_alpha, "qwen3-8b o_proj")
+    g = np.random.default_rng(5)
+    mi = np.concatenate([g.integers(0, w.M, 4096), [0, w.M - 1]])
+    ni = np.concatenate([g.integers(0, N, 4096), [N - 1, 0]])
+    pref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
+    _check(nv, oracle_mod, A, W, y_alpha, "qwen3-8b o_proj", pairs=(mi, ni, pref))
 
 
 def test_quant_out_k_zero_and_errors(nv):
     import torch
-
-    from nvfp4_prefill_gemm_amd.binding import Nvfp4Error
 
     say("gemm quant out K=0 / errors")
     z = torch.empty((4, 0), dtype=torch.uint8, device="cuda")
@@ -112,5 +118,11 @@ def test_quant_out_k_zero_and_errors(nv):
     s = torch.zeros((4, 1), dtype=torch.uint8, device="cuda")
     w = torch.zeros((24, 8), dtype=torch.uint8, device="cuda")
     ws = torch.zeros((24, 1), dtype=torch.uint8, device="cuda")
-    with pytest.raises(Nvfp4Error, match="multiple of 16"):
+    # the binding refuses N % 16 != 0 before the call; the C ABI refuses it too
+    with pytest.raises(ValueError, match="multiple of 16"):
         nv.nvfp4_gemm_quant_out(a, s, one, w, ws, one, one)
+    yc2 = torch.zeros((4, 12), dtype=torch.uint8, device="cuda")
+    ys2 = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    rc = nv.lib().nvfp4_gemm_quant_out(nv._ptr(a), nv._ptr(s), nv._ptr(one), nv._ptr(w), nv._ptr(ws), nv._ptr(one),
+                                       4, 24, 16, nv._ptr(yc2), nv._ptr(ys2), nv._ptr(one), nv._stream(None))
+    assert rc == nv.NVFP4_EINVAL and "multiple of 16" in nv.last_error()
