@@ -85,6 +85,23 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                    size_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4_quantize for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and checks as nvfp4_quantize, without a workspace:
+ * in NVFP4_ALPHA_DYNAMIC mode the amax partials live in a scratch array
+ * inside the library, 4 KB (1024 partial maxima) per GPU, held by every GPU
+ * the library runs on until the process ends.  Every tensor size that
+ * nvfp4_quantize accepts fits it (the amax pass never writes more than 1024
+ * partials); a larger count would be refused with NVFP4_EUNSUPPORTED.  The
+ * call allocates nothing.  All calls on one GPU share that GPU's array and
+ * leave their partials in it: calls that overlap on one GPU (on different
+ * streams, or from different threads) race and must be ordered by the
+ * caller.
+ */
+int nvfp4_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                           uint8_t *scales, float *alpha, int alpha_mode, void *stream);
+
+/*
  * NVFP4 x NVFP4 GEMM (the W4A4 prefill linear layer; Mix-Quant Section 3.3
  * and Section 4.2 "Prefilling Stage Speedup"):
  *   Y[m, n] = sum_k xhatA[m, k] * xhatW[n, k],   xhat = alpha * sigma * q (Eq. 2)

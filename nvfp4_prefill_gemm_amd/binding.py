@@ -27,6 +27,7 @@ _SIGNATURES = {
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
+    "nvfp4_quantize_noalloc": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I, _P]),
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
     "nvfp4_gemm_quant_out": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64]),
@@ -200,6 +201,26 @@ def nvfp4_quantize(x: torch.Tensor, codes: torch.Tensor | None = None, scales: t
                               NVFP4_ALPHA_STATIC if static_alpha else NVFP4_ALPHA_DYNAMIC, _ptr(workspace),
                               _nbytes(workspace), _stream(stream))
     _check("nvfp4_quantize", rc)
+    return codes, scales, alpha
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor,
+                           static_alpha: bool = False, stream=None):
+    """nvfp4_quantize into caller-provided outputs without a workspace: the
+    dynamic tensor scale's partial maxima use the library's per-GPU scratch
+    array (calls that overlap on one GPU race)."""
+    _mat(x, "x", torch.bfloat16, contiguous=False)
+    rows, cols = x.shape
+    if cols % 16:
+        raise ValueError(f"x: cols = {cols} must be a multiple of 16")
+    _mat(codes, "codes", torch.uint8, rows, cols // 2)
+    _mat(scales, "scales", torch.uint8, rows, cols // 16)
+    _alpha(alpha, "alpha")
+    _same_device(("x", x), ("codes", codes), ("scales", scales), ("alpha", alpha))
+    rc = lib().nvfp4_quantize_noalloc(_ptr(x), rows, cols, x.stride(0), _ptr(codes), _ptr(scales), _ptr(alpha),
+                                      NVFP4_ALPHA_STATIC if static_alpha else NVFP4_ALPHA_DYNAMIC,
+                                      _stream(stream))
+    _check("nvfp4_quantize_noalloc", rc)
     return codes, scales, alpha
 
 

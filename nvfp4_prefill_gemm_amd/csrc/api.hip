@@ -49,22 +49,9 @@ int check_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *alpha,
     return NVFP4_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
-
-const char *nvfp4_last_error(void) { return g_err; }
-
-size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) {
-    if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)nvfp4::amax_parts(rows, cols) * sizeof(uint32_t);
-}
-
-int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes, uint8_t *scales,
-                   float *alpha, int alpha_mode, void *workspace, size_t workspace_bytes, void *stream) {
-    const char *fn = "nvfp4_quantize";
+int quantize_impl(const char *fn, const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                  uint8_t *scales, float *alpha, int alpha_mode, void *workspace, size_t workspace_bytes,
+                  bool use_scratch, void *stream) {
     if (rows < 0 || cols < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
     if (cols % 16 != 0) return fail(NVFP4_EINVAL, "%s: cols (%lld) must be a multiple of 16", fn, (long long)cols);
     if (alpha_mode != NVFP4_ALPHA_DYNAMIC && alpha_mode != NVFP4_ALPHA_STATIC)
@@ -80,6 +67,15 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
     hipStream_t s = as_stream(stream);
     const int dyn = alpha_mode == NVFP4_ALPHA_DYNAMIC;
     const int nparts = nvfp4::amax_parts(rows, cols);
+    if (dyn && use_scratch) {
+        uint32_t *p = nullptr;
+        size_t bytes = 0;
+        if (int rc = hip_status(nvfp4::quantize_scratch(&p, &bytes), "scratch lookup")) return rc;
+        if ((size_t)nparts * sizeof(uint32_t) > bytes)
+            return fail(NVFP4_EUNSUPPORTED, "%s: %d amax partials exceed the %zu-byte scratch", fn, nparts, bytes);
+        workspace = p;
+        workspace_bytes = bytes;
+    }
     if (dyn) {
         const size_t need = (size_t)nparts * sizeof(uint32_t);
         if (!workspace || workspace_bytes < need)
@@ -93,6 +89,31 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
     return hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, rows, cols, ld_x, codes, scales, alpha, dyn,
                                              (const uint32_t *)workspace, nparts, s),
                       "quantize kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char *nvfp4_last_error(void) { return g_err; }
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)nvfp4::amax_parts(rows, cols) * sizeof(uint32_t);
+}
+
+int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes, uint8_t *scales,
+                   float *alpha, int alpha_mode, void *workspace, size_t workspace_bytes, void *stream) {
+    return quantize_impl("nvfp4_quantize", x_bf16, rows, cols, ld_x, codes, scales, alpha, alpha_mode, workspace,
+                         workspace_bytes, false, stream);
+}
+
+int nvfp4_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                           uint8_t *scales, float *alpha, int alpha_mode, void *stream) {
+    return quantize_impl("nvfp4_quantize_noalloc", x_bf16, rows, cols, ld_x, codes, scales, alpha, alpha_mode,
+                         nullptr, 0, true, stream);
 }
 
 int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha, const uint8_t *w_codes,

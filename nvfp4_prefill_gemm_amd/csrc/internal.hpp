@@ -34,6 +34,10 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials,
                            int nparts, hipStream_t s);
 
+// Device address and size of this device's scratch array for the amax
+// partials of nvfp4_quantize_noalloc (looked up once per device).
+hipError_t quantize_scratch(uint32_t **ptr, size_t *bytes);
+
 // alpha from partials only (fused path, dynamic mode).
 hipError_t launch_alpha_from_partials(const uint32_t *partials, int nparts, float *alpha, hipStream_t s);
 

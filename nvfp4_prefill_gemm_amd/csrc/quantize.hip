@@ -247,6 +247,34 @@ int quant_grid(int64_t rows, int64_t cols) {
 
 }  // namespace
 
+// Scratch of the allocation-free entry point (nvfp4_quantize_noalloc): the
+// dynamic tensor scale's per-workgroup partial maxima, at most kMaxParts of
+// them (4 KB).  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it.  The partials need no
+// clearing: the amax pass writes each entry the quantize pass reads.
+static __device__ __align__(256) uint32_t scratch[kMaxParts];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current.  Host code never passes `scratch` itself
+// to a kernel: its host-side name is a stand-in, not a device address.
+hipError_t quantize_scratch(uint32_t **ptr, size_t *bytes) {
+    constexpr int kDevs = 64;
+    static std::atomic<uint32_t *> cache[kDevs];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    uint32_t *p = dev >= 0 && dev < kDevs ? cache[dev].load(std::memory_order_acquire) : nullptr;
+    if (!p) {
+        e = hipGetSymbolAddress((void **)&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        if (dev >= 0 && dev < kDevs) cache[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
+
 int amax_parts(int64_t rows, int64_t cols) {
     int64_t g = (quant_items(rows, cols) + kWaves - 1) / kWaves;
     if (g > kMaxParts) g = kMaxParts;
