@@ -292,12 +292,12 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
     # repeated
     if sweep:
         def timed_ms(step):
-            for _ in range(2):
-                step()
+            for i in range(ROT):
+                step(i)
             torch.cuda.synchronize()
             s.record()
-            for _ in range(reps):
-                step()
+            for i in range(reps):
+                step(i)
             e.record()
             torch.cuda.synchronize()
             return s.elapsed_time(e) / reps
@@ -320,35 +320,50 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
                                                      dtype=torch.uint8, device=dev),
                                      y=torch.empty((Ms, L["N"]), dtype=torch.bfloat16, device=dev)))
 
-                def nv_step():
-                    for L, B in zip(layers, bufs):
+                # the weights rotate over the same copies as in the headline
+                # step (three sets: the NVFP4 weights of one set would
+                # otherwise stay in the Infinity Cache from rep to rep)
+                def nv_step(i):
+                    for L, B in zip(sets[i % ROT], bufs):
                         nv.nvfp4_quantize(B["x"], B["ac"], B["asc"], B["aal"], workspace=B["wsb"])
-                        nv.nvfp4_gemm(B["ac"], B["asc"], B["aal"], L["wc"], L["ws"], L["wa"], out=B["y"])
+                        nv.nvfp4_gemm(B["ac"], B["asc"], B["aal"], L["wc"], L["ws"], L["wa"], out=B["y"],
+                                      workspace=False)
 
-                def bf_step():
-                    for L, B in zip(layers, bufs):
-                        nv.bf16_gemm(B["x"], L["w_bf16"], out=B["y"])
+                def bf_step(i):
+                    for L, B in zip(sets[i % ROT], bufs):
+                        nv.bf16_gemm(B["x"], L["w_bf16"], out=B["y"], workspace=False)
                 t4, t16 = timed_ms(nv_step), timed_ms(bf_step)
                 del bufs
             sw[str(Ms)] = {"nvfp4_tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
                            "bf16_tflops": round(fl / (t16 * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(t16 / t4, 3)}
         out["prefill_sweep"] = sw
 
-    # fused quantize-in-GEMM prologue (dynamic alpha: amax pass + fused GEMM)
-    def fused_step():
-        for L in layers:
+    # nvfp4_quant_gemm (BF16 activations in, dynamic alpha), on the same
+    # rotated sets: with its full workspace it quantizes once into the
+    # workspace and runs the NVFP4 GEMM; with only the amax partials' workspace
+    # the tile kernel quantizes in its operand staging (every column tile
+    # again), reported as fused_prologue_tflops
+    qg_ws = [torch.empty(nv.quant_gemm_workspace_size(M, L["N"], L["K"]), dtype=torch.uint8, device=dev)
+             for L in layers]
+
+    def fused_step(i, full=True):
+        for j, L in enumerate(sets[i % ROT]):
             nv.nvfp4_quant_gemm(L["x"], L["wc"], L["ws"], L["wa"], a_alpha=L["aal"], out=L["y"],
-                                workspace=L["ws_buf"])
-    for _ in range(2):
-        fused_step()
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
-        fused_step()
-    e.record()
-    torch.cuda.synchronize()
-    fused_ms = s.elapsed_time(e) / reps
-    out["fused_tflops"] = round(flops_step / (fused_ms * 1e-3) / 1e12, 2)
+                                workspace=qg_ws[j] if full else L["ws_buf"])
+
+    def fused_ms_of(full):
+        for i in range(ROT):
+            fused_step(i, full)
+        torch.cuda.synchronize()
+        s.record()
+        for i in range(reps):
+            fused_step(i, full)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+    out["fused_tflops"] = round(flops_step / (fused_ms_of(True) * 1e-3) / 1e12, 2)
+    out["fused_prologue_tflops"] = round(flops_step / (fused_ms_of(False) * 1e-3) / 1e12, 2)
+    del qg_ws
 
     # NVFP4 GEMM whose epilogue quantizes Y to NVFP4 for the next layer
     # (static output scale), same layers and activations
@@ -433,10 +448,12 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
     for Md in wl.PHASE_SPLIT_DECODE_M:
         xs = [torch.randn((Md, L["K"]), device=dev).to(torch.bfloat16) for L in layers]
         ys = [torch.empty((Md, L["N"]), dtype=torch.bfloat16, device=dev) for L in layers]
+        wsd = [torch.empty(max(nv.bf16_gemm_workspace_size(Md, L["N"], L["K"]), 16), dtype=torch.uint8, device=dev)
+               for L in layers]
 
         def dec_step(c):
             for i, L in enumerate(layers):
-                nv.bf16_gemm(xs[i], copies[c][i], out=ys[i])
+                nv.bf16_gemm(xs[i], copies[c][i], out=ys[i], workspace=wsd[i])
         us = graph_us(dec_step, 2, 20)
         nbytes = sum(2 * L["N"] * L["K"] + 2 * Md * L["K"] + 2 * Md * L["N"] for L in layers)
         decode[str(Md)] = {"us_per_step": round(us, 1), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
@@ -454,24 +471,18 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
     for Md in wl.PHASE_SPLIT_DECODE_M:
         xs = [torch.randn((Md, L["K"]), device=dev).to(torch.bfloat16) for L in layers]
         ys = [torch.empty((Md, L["N"]), dtype=torch.bfloat16, device=dev) for L in layers]
-        qa = [(torch.empty((Md, L["K"] // 2), dtype=torch.uint8, device=dev),
-               torch.empty((Md, L["K"] // 16), dtype=torch.uint8, device=dev),
-               torch.empty(1, dtype=torch.float32, device=dev),
-               torch.empty(max(nv.quantize_workspace_size(Md, L["K"]), 4), dtype=torch.uint8, device=dev))
-              for L in layers]
-
-        # single-token decode: one kernel per layer, the activation quantized
-        # inside the decode GEMM (nvfp4_quant_gemm); larger batches quantize once
-        fused = [Md == 1 for L in layers]
+        # one nvfp4_quant_gemm per layer: BF16 activations in, dynamic alpha;
+        # the library quantizes the batch inside the decode kernel (small
+        # batches) or into the workspace before it
+        qa = [(torch.empty(1, dtype=torch.float32, device=dev),
+               torch.empty(max(nv.quant_gemm_workspace_size(Md, L["N"], L["K"]), 16), dtype=torch.uint8,
+                           device=dev)) for L in layers]
+        fused = [Md * L["K"] <= 196608 and Md <= 2 for L in layers]
 
         def dec4_step(c):
             for i, L in enumerate(layers):
-                ac, asc, aal, wsb = qa[i]
-                if fused[i]:
-                    nv.nvfp4_quant_gemm(xs[i], *wq[c][i], a_alpha=aal, out=ys[i], workspace=wsb)
-                else:
-                    nv.nvfp4_quantize(xs[i], ac, asc, aal, workspace=wsb)
-                    nv.nvfp4_gemm(ac, asc, aal, *wq[c][i], out=ys[i])
+                aal, wsb = qa[i]
+                nv.nvfp4_quant_gemm(xs[i], *wq[c][i], a_alpha=aal, out=ys[i], workspace=wsb)
         us = graph_us(dec4_step, 4, 20)
         nbytes = sum(L["N"] * L["K"] * 9 // 16 + 2 * Md * L["K"] + Md * L["K"] * 9 // 16 + 2 * Md * L["N"]
                      for L in layers)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 enum {
     NVFP4_OK = 0,
@@ -69,6 +69,10 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 
 /*
  * BF16 -> NVFP4 quantization (Mix-Quant Section 3.3, Eq. 3 then Eq. 2).
+ * Dynamic alpha: an amax pass writes per-workgroup partial maxima to the
+ * workspace, then the quantize pass runs; a tensor of at most 131072
+ * elements (a decode batch) takes one launch, every workgroup forming the
+ * amax itself, and leaves the workspace untouched.
  *   x_bf16   [rows, ld_x] BF16, 16-byte aligned, ld_x % 8 == 0
  *   rows>=0, cols >= 0 with cols % 16 == 0 (one block is 16 elements)
  *   codes    [rows, cols/2] uint8 out, 16-byte aligned
@@ -101,6 +105,11 @@ int nvfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
 int nvfp4_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
                            uint8_t *scales, float *alpha, int alpha_mode, void *stream);
 
+/* Bytes of device workspace nvfp4_gemm uses at these sizes for its fastest
+ * kernels (0: none).  Decode shapes split K over workgroups and keep FP32
+ * partial tiles [S][M][N] there. */
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
 /*
  * NVFP4 x NVFP4 GEMM (the W4A4 prefill linear layer; Mix-Quant Section 3.3
  * and Section 4.2 "Prefilling Stage Speedup"):
@@ -110,13 +119,20 @@ int nvfp4_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int64
  *   K % 16 == 0; M, N >= 0; code arrays 16-byte aligned, scale arrays 4-byte aligned
  *   out [M, ld_out] FP32 (NVFP4_OUT_F32) or BF16 (NVFP4_OUT_BF16, nearest-even),
  *   ld_out >= N.  Accumulation is FP32; each product q*sigma is exact.
- * At decode shapes (M <= 64, K % 32 == 0, K < 2^24; the uniform-NVFP4 and FP4-decode
- * variants of Mix-Quant Section 4) a split-K kernel streams the weights;
- * otherwise a tile kernel runs.  Both sum in FP32 but in different orders.
+ *   workspace: NULL, or 16-byte aligned device scratch of workspace_bytes;
+ *   contents undefined on entry and exit; a call that overlaps another use of
+ *   the same workspace races.  With at least nvfp4_gemm_workspace_size(M, N, K)
+ *   bytes the decode kernels split K over workgroups (S slices: partial tiles
+ *   summed in slice order by a second kernel); with less they run unsplit.
+ * At decode shapes (M <= 64, K % 32 == 0, K < 2^24; the uniform-NVFP4 and
+ * FP4-decode variants of Mix-Quant Section 4) the decode kernels stream the
+ * weights; otherwise a tile kernel runs.  These kernels, and split and unsplit
+ * runs, sum in FP32 but in different orders.
  */
 int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
-               int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out, void *stream);
+               int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out, void *workspace,
+               size_t workspace_bytes, void *stream);
 
 /*
  * NVFP4 x NVFP4 GEMM whose output is itself NVFP4, for the next linear layer
@@ -136,28 +152,45 @@ int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const 
                          int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales, const float *y_alpha,
                          void *stream);
 
-/* Bytes of device workspace nvfp4_quant_gemm needs (dynamic-alpha mode). */
-size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t K);
+/* Bytes of device workspace nvfp4_quant_gemm uses at these sizes for its
+ * fastest path (see nvfp4_quant_gemm). */
+size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
- * Fused prefill linear: BF16 activations are quantized to NVFP4 inside the
- * GEMM's operand staging (Mix-Quant Section 3.3: quantization, dequantization
- * and the matrix product fused by the backend).  No codes or scales are
- * written.  For M <= 16 with M * K <= 196608 and K % 32 == 0 a decode kernel
- * quantizes the batch into LDS (every workgroup forms the dynamic alpha
- * itself); otherwise an amax pass precedes a tile kernel that quantizes in its
- * operand staging.  The result equals nvfp4_quantize followed by nvfp4_gemm
- * bit for bit whenever both run decode kernels (the condition above) or both
- * run tile kernels (M > 64 or K % 32 != 0); in between they sum in different
- * orders (both within FP32 rounding of the exact product).
+ * Prefill linear from BF16 activations: quantization to NVFP4 and the GEMM in
+ * one call (Mix-Quant Section 3.3: quantization, dequantization and the
+ * matrix product fused by the backend).
  *   x_bf16 [M, ld_x] BF16 (16-byte aligned, ld_x % 8 == 0), K % 16 == 0
  *   a_alpha float[1]: written (dynamic) or read (static) as in nvfp4_quantize
  *   weights, out, out_dtype, ld_out as in nvfp4_gemm
+ *   workspace: 16-byte aligned device scratch (contents undefined on entry and
+ *   exit); dynamic alpha needs at least nvfp4_quantize_workspace_size(M, K)
+ *   bytes (NVFP4_EWORKSPACE otherwise).
+ * Paths, by shape and workspace:
+ *   - M <= 2, M * K <= 196608, K % 32 == 0: one decode kernel quantizes the
+ *     batch into LDS in every workgroup (each forms the dynamic alpha itself)
+ *     and streams the weights (larger batches measured faster quantized once);
+ *   - otherwise, with nvfp4_quant_gemm_workspace_size(M, N, K) bytes: the
+ *     quantizer writes codes and scales into the workspace and nvfp4_gemm's
+ *     kernels run on them (one quantization per activation element; the
+ *     in-prologue variant below repeats it for every column tile and measured
+ *     slower at every prefill size);
+ *   - otherwise: a tile kernel quantizes the activations in its operand
+ *     staging (after an amax pass for a dynamic alpha).
+ * Results equal nvfp4_quantize followed by nvfp4_gemm (given the workspace
+ * sizes of both queries) bit for bit, except between the third path and a
+ * decode kernel, or the first path and the tile kernel (M > 64 or
+ * K % 32 != 0): there the two sum in different orders (both within FP32
+ * rounding of the exact product).
  */
 int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha_mode,
                      const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                      int64_t M, int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace bf16_gemm uses at these sizes for its fastest
+ * kernels (0: none); as nvfp4_gemm_workspace_size. */
+size_t bf16_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
  * BF16 GEMM of the high-precision decode path and the prefill baseline
@@ -165,11 +198,12 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
  * decode path keeps the original BF16 model; Section 4.2: the BF16 baseline).
  *   Y[M, N] = A[M, K] * W[N, K]^T, FP32 accumulation
  *   a_bf16 [M, K] and w_bf16 [N, K] contiguous, 16-byte aligned, K % 8 == 0
- *   out [M, ld_out] FP32 or BF16.  Small M (decode batches) uses a
- *   bandwidth-oriented kernel; large M the MFMA tile kernel.
+ *   out [M, ld_out] FP32 or BF16.  Small M (decode batches, M <= 64) uses a
+ *   bandwidth-oriented kernel, split over K with a large enough workspace
+ *   (as in nvfp4_gemm); large M the MFMA tile kernel.
  */
 int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int64_t K, void *out,
-              int out_dtype, int64_t ld_out, void *stream);
+              int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * MXFP4 (Mix-Quant Section 3.3 names it as the coarser microscaling format

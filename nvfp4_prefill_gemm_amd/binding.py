@@ -28,11 +28,13 @@ _SIGNATURES = {
     "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
     "nvfp4_quantize_noalloc": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I, _P]),
-    "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
+    "nvfp4_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "nvfp4_gemm_quant_out": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
-    "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quant_gemm": (_I, [_P, _I64, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
-    "bf16_gemm": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
+    "bf16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "bf16_gemm": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "mxfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxfp4_gemm": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
 }
@@ -239,17 +241,39 @@ def _nvfp4_operands(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha):
     return M, N, K
 
 
+def gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_gemm_workspace_size(M, N, K))
+
+
+def bf16_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().bf16_gemm_workspace_size(M, N, K))
+
+
+def _workspace(workspace, nbytes: int, dev):
+    """The caller's workspace, or a fresh one of nbytes (None when 0).  Pass
+    workspace=False to run without one."""
+    if workspace is False:
+        return None
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else None
+    return _tensor(workspace, "workspace")
+
+
 def nvfp4_gemm(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, out: torch.Tensor | None = None,
-               out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
-    """Y [M, N] = dequant(A) @ dequant(W)^T from NVFP4 operands."""
+               out_dtype=torch.bfloat16, workspace=None, stream=None) -> torch.Tensor:
+    """Y [M, N] = dequant(A) @ dequant(W)^T from NVFP4 operands.  workspace:
+    device scratch (default: gemm_workspace_size bytes; False: none)."""
     M, N, K = _nvfp4_operands(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
     _out(out, "out", M, N)
     _same_device(("a_codes", a_codes), ("a_scales", a_scales), ("a_alpha", a_alpha), ("w_codes", w_codes),
-                 ("w_scales", w_scales), ("w_alpha", w_alpha), ("out", out))
+                 ("w_scales", w_scales), ("w_alpha", w_alpha), ("out", out),
+                 ("workspace", workspace if isinstance(workspace, torch.Tensor) else None))
+    workspace = _workspace(workspace, gemm_workspace_size(M, N, K) if workspace is None else 0, a_codes.device)
     rc = lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_alpha), _ptr(w_codes), _ptr(w_scales),
-                          _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _stream(stream))
+                          _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _ptr(workspace),
+                          _nbytes(workspace), _stream(stream))
     _check("nvfp4_gemm", rc)
     return out
 
@@ -278,8 +302,8 @@ def nvfp4_gemm_quant_out(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha,
     return y_codes, y_scales
 
 
-def quant_gemm_workspace_size(M: int, K: int) -> int:
-    return int(lib().nvfp4_quant_gemm_workspace_size(M, K))
+def quant_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_quant_gemm_workspace_size(M, N, K))
 
 
 def nvfp4_quant_gemm(x: torch.Tensor, w_codes, w_scales, w_alpha, a_alpha: torch.Tensor | None = None,
@@ -306,8 +330,8 @@ def nvfp4_quant_gemm(x: torch.Tensor, w_codes, w_scales, w_alpha, a_alpha: torch
         _tensor(workspace, "workspace")
     _same_device(("x", x), ("w_codes", w_codes), ("w_scales", w_scales), ("w_alpha", w_alpha), ("out", out),
                  ("a_alpha", a_alpha), ("workspace", workspace))
-    if not static_alpha and workspace is None:
-        workspace = torch.empty(max(quant_gemm_workspace_size(M, K), 4), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(quant_gemm_workspace_size(M, N, K), 16), dtype=torch.uint8, device=x.device)
     rc = lib().nvfp4_quant_gemm(_ptr(x), x.stride(0), _ptr(a_alpha),
                                 NVFP4_ALPHA_STATIC if static_alpha else NVFP4_ALPHA_DYNAMIC, _ptr(w_codes),
                                 _ptr(w_scales), _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0),
@@ -317,8 +341,9 @@ def nvfp4_quant_gemm(x: torch.Tensor, w_codes, w_scales, w_alpha, a_alpha: torch
 
 
 def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
-              stream=None) -> torch.Tensor:
-    """Y [M, N] = A [M, K] @ W [N, K]^T in BF16 with FP32 accumulation."""
+              workspace=None, stream=None) -> torch.Tensor:
+    """Y [M, N] = A [M, K] @ W [N, K]^T in BF16 with FP32 accumulation.
+    workspace: device scratch (default: bf16_gemm_workspace_size bytes; False: none)."""
     _mat(a, "a", torch.bfloat16)
     M, K = a.shape
     _mat(w, "w", torch.bfloat16, cols=K)
@@ -326,8 +351,11 @@ def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _out(out, "out", M, N)
-    _same_device(("a", a), ("w", w), ("out", out))
-    rc = lib().bf16_gemm(_ptr(a), _ptr(w), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _stream(stream))
+    _same_device(("a", a), ("w", w), ("out", out),
+                 ("workspace", workspace if isinstance(workspace, torch.Tensor) else None))
+    workspace = _workspace(workspace, bf16_gemm_workspace_size(M, N, K) if workspace is None else 0, a.device)
+    rc = lib().bf16_gemm(_ptr(a), _ptr(w), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _ptr(workspace),
+                         _nbytes(workspace), _stream(stream))
     _check("bf16_gemm", rc)
     return out
 

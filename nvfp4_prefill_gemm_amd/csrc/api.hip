@@ -49,6 +49,35 @@ int check_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *alpha,
     return NVFP4_OK;
 }
 
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// nvfp4_quant_gemm's workspace when it quantizes into the workspace and then
+// runs the NVFP4 GEMM: codes [M, K/2], scales [M, K/16], the amax partials
+// (dynamic alpha) and the GEMM's split-K partials, each 256-byte aligned.
+struct QgLayout {
+    size_t codes, scales, parts, split, total;
+};
+QgLayout qg_layout(int64_t M, int64_t N, int64_t K, bool dyn) {
+    QgLayout l;
+    l.codes = 0;
+    l.scales = align256((size_t)M * (size_t)(K / 2));
+    l.parts = l.scales + align256((size_t)M * (size_t)(K / 16));
+    l.split = l.parts + (dyn ? align256((size_t)nvfp4::amax_parts(M, K) * sizeof(uint32_t)) : 0);
+    size_t split_bytes = 0;
+    if (M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % 32 == 0)
+        split_bytes = nvfp4::decode_workspace_bytes(nvfp4::DECODE_NVFP4, M, N, K);
+    l.total = l.split + split_bytes;
+    return l;
+}
+
+bool fused_decode_shape(int64_t M, int64_t K) {
+    return M <= nvfp4::kFusedDecodeMaxM && M * K <= nvfp4::kFusedDecodeMaxElems && K % 32 == 0;
+}
+
+bool decode_shape(int64_t M, int64_t K, int kmult) {
+    return M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % kmult == 0;
+}
+
 int quantize_impl(const char *fn, const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
                   uint8_t *scales, float *alpha, int alpha_mode, void *workspace, size_t workspace_bytes,
                   bool use_scratch, void *stream) {
@@ -81,10 +110,11 @@ int quantize_impl(const char *fn, const void *x_bf16, int64_t rows, int64_t cols
         if (!workspace || workspace_bytes < need)
             return fail(NVFP4_EWORKSPACE, "%s: dynamic alpha needs %zu workspace bytes", fn, need);
         if (!aligned(workspace, 4)) return fail(NVFP4_EINVAL, "%s: workspace is misaligned", fn);
-        int rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, rows, cols, ld_x,
-                                                        (uint32_t *)workspace, nparts, s),
-                            "amax kernel");
-        if (rc) return rc;
+        if (!nvfp4::quantize_self_amax(rows, cols))
+            if (int rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, rows, cols, ld_x,
+                                                                (uint32_t *)workspace, nparts, s),
+                                    "amax kernel"))
+                return rc;
     }
     return hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, rows, cols, ld_x, codes, scales, alpha, dyn,
                                              (const uint32_t *)workspace, nparts, s),
@@ -116,9 +146,14 @@ int nvfp4_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int64
                          nullptr, 0, true, stream);
 }
 
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || !decode_shape(M, K, 32)) return 0;
+    return nvfp4::decode_workspace_bytes(nvfp4::DECODE_NVFP4, M, N, K);
+}
+
 int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha, const uint8_t *w_codes,
                const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K, void *out,
-               int out_dtype, int64_t ld_out, void *stream) {
+               int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream) {
     const char *fn = "nvfp4_gemm";
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
     if (K % 16 != 0) return fail(NVFP4_EINVAL, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
@@ -130,9 +165,10 @@ int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_a
     if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
     if ((rc = check_nvfp4(a_codes, a_scales, a_alpha, "A", fn))) return rc;
     if ((rc = check_nvfp4(w_codes, w_scales, w_alpha, "W", fn))) return rc;
-    if (M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % 32 == 0)
+    if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    if (decode_shape(M, K, 32))
         return hip_status(nvfp4::launch_skinny_nvfp4(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K,
-                                                     out, out_dtype, ld_out, s),
+                                                     out, out_dtype, ld_out, workspace, workspace_bytes, s),
                           "nvfp4 decode kernel");
     return hip_status(nvfp4::launch_gemm_nvfp4(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out,
                                                out_dtype, ld_out, s),
@@ -163,7 +199,15 @@ int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const 
                       "nvfp4 gemm kernel (quantized output)");
 }
 
-size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t K) { return nvfp4_quantize_workspace_size(M, K); }
+size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    const size_t parts = nvfp4_quantize_workspace_size(M, K);  // the minimum with a dynamic alpha
+    if (fused_decode_shape(M, K)) {
+        const size_t split = nvfp4::decode_workspace_bytes(nvfp4::DECODE_FUSED, M, N, K);
+        return split > parts ? split : parts;
+    }
+    return qg_layout(M, N, K, true).total;
+}
 
 int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha_mode, const uint8_t *w_codes,
                      const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K, void *out,
@@ -183,19 +227,49 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
     if (ld_x < K || ld_x % 8 != 0) return fail(NVFP4_EINVAL, "%s: ld_x must be >= K and a multiple of 8", fn);
     if (!aligned(x_bf16, 16)) return fail(NVFP4_EINVAL, "%s: x must be 16-byte aligned", fn);
     if ((rc = check_nvfp4(w_codes, w_scales, w_alpha, "W", fn))) return rc;
-    if (alpha_mode == NVFP4_ALPHA_DYNAMIC) {
+    const bool dyn = alpha_mode == NVFP4_ALPHA_DYNAMIC;
+    if (dyn) {
         const int nparts = nvfp4::amax_parts(M, K);
         const size_t need = (size_t)nparts * sizeof(uint32_t);
         if (!workspace || workspace_bytes < need)
             return fail(NVFP4_EWORKSPACE, "%s: dynamic alpha needs %zu workspace bytes", fn, need);
-        if (!aligned(workspace, 4)) return fail(NVFP4_EINVAL, "%s: workspace is misaligned", fn);
     }
-    if (M <= nvfp4::kFusedDecodeMaxM && M * K <= nvfp4::kFusedDecodeMaxElems && K % 32 == 0)
-        return hip_status(nvfp4::launch_skinny_fused((const uint16_t *)x_bf16, ld_x, a_alpha,
-                                                     alpha_mode == NVFP4_ALPHA_DYNAMIC, w_codes, w_scales, w_alpha, M,
-                                                     N, K, out, out_dtype, ld_out, s),
+    if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    // decode batches: one kernel quantizes the batch into LDS and runs the decode GEMM
+    if (fused_decode_shape(M, K))
+        return hip_status(nvfp4::launch_skinny_fused((const uint16_t *)x_bf16, ld_x, a_alpha, dyn, w_codes, w_scales,
+                                                     w_alpha, M, N, K, out, out_dtype, ld_out, workspace,
+                                                     workspace_bytes, s),
                           "fused decode kernel");
-    if (alpha_mode == NVFP4_ALPHA_DYNAMIC) {
+    // otherwise quantize once into the workspace and run the NVFP4 GEMM: the
+    // tile kernel's in-prologue quantization repeats for every column tile
+    // and measured slower at every prefill size
+    const QgLayout l = qg_layout(M, N, K, dyn);
+    uint8_t *wsb = (uint8_t *)workspace;
+    if (workspace && workspace_bytes >= l.split) {
+        uint8_t *codes = wsb + l.codes, *scales = wsb + l.scales;
+        const int nparts = nvfp4::amax_parts(M, K);
+        if (dyn && !nvfp4::quantize_self_amax(M, K) &&
+            (rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, M, K, ld_x,
+                                                         (uint32_t *)(wsb + l.parts), nparts, s),
+                             "amax kernel")))
+            return rc;
+        if ((rc = hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha, dyn,
+                                                    (const uint32_t *)(wsb + l.parts), nparts, s),
+                             "quantize kernel")))
+            return rc;
+        if (decode_shape(M, K, 32))
+            return hip_status(nvfp4::launch_skinny_nvfp4(codes, scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K,
+                                                         out, out_dtype, ld_out, wsb + l.split,
+                                                         workspace_bytes - l.split, s),
+                              "nvfp4 decode kernel");
+        return hip_status(nvfp4::launch_gemm_nvfp4(codes, scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out,
+                                                   out_dtype, ld_out, s),
+                          "nvfp4 gemm kernel");
+    }
+    // a workspace too small for the quantized activations: the tile kernel
+    // quantizes in its operand staging
+    if (dyn) {
         const int nparts = nvfp4::amax_parts(M, K);
         if ((rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, M, K, ld_x, (uint32_t *)workspace,
                                                          nparts, s),
@@ -210,8 +284,13 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
                       "fused gemm kernel");
 }
 
+size_t bf16_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || !decode_shape(M, K, 8)) return 0;
+    return nvfp4::decode_workspace_bytes(nvfp4::DECODE_BF16, M, N, K);
+}
+
 int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int64_t K, void *out, int out_dtype,
-              int64_t ld_out, void *stream) {
+              int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream) {
     const char *fn = "bf16_gemm";
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
     if (K % 8 != 0) return fail(NVFP4_EUNSUPPORTED, "%s: K (%lld) must be a multiple of 8", fn, (long long)K);
@@ -223,9 +302,10 @@ int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int6
     if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
     if (!a_bf16 || !w_bf16) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
     if (!aligned(a_bf16, 16) || !aligned(w_bf16, 16)) return fail(NVFP4_EINVAL, "%s: A and W must be 16-byte aligned", fn);
-    if (M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK)
+    if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    if (decode_shape(M, K, 8))
         return hip_status(nvfp4::launch_skinny_bf16((const uint16_t *)a_bf16, (const uint16_t *)w_bf16, M, N, K, out,
-                                                    out_dtype, ld_out, s),
+                                                    out_dtype, ld_out, workspace, workspace_bytes, s),
                           "skinny bf16 kernel");
     return hip_status(nvfp4::launch_gemm_bf16((const uint16_t *)a_bf16, (const uint16_t *)w_bf16, M, N, K, out,
                                               out_dtype, ld_out, s),

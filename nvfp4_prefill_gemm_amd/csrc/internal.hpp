@@ -29,7 +29,14 @@ int amax_parts(int64_t rows, int64_t cols);
 hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
                                 uint32_t *partials, int nparts, hipStream_t s);
 
-// dynamic != 0: alpha = max(partials[0..nparts)) / 2688 is written to *alpha.
+// Small tensors (rows * cols <= kSelfAmaxMaxElems, e.g. decode batches) take
+// a single launch in dynamic mode: every workgroup of the quantize pass reads
+// the whole tensor for its amax, and no amax pass (nor its partials) is used.
+constexpr int64_t kSelfAmaxMaxElems = int64_t(1) << 17;
+bool quantize_self_amax(int64_t rows, int64_t cols);
+
+// dynamic != 0: alpha = amax / 2688 is written to *alpha, the amax taken from
+// partials[0..nparts), or from the tensor itself when quantize_self_amax().
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials,
                            int nparts, hipStream_t s);
@@ -63,29 +70,42 @@ hipError_t launch_gemm_fused(const uint16_t *x, int64_t ld_x, const float *a_alp
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K,
                             void *out, int out_type, int64_t ld_out, hipStream_t s);
 
-hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K,
-                              void *out, int out_type, int64_t ld_out, hipStream_t s);
+// Decode kernels (M <= kSkinnyMaxM): a workgroup owns ng 16-column groups and
+// one of s K slices; s > 1 writes FP32 partials [s][M][N] to a workspace and
+// a reduction kernel sums them in slice order.
+enum DecodeKind { DECODE_BF16 = 0, DECODE_NVFP4 = 1, DECODE_FUSED = 2 };
+struct DecodePlan {
+    int ng, waves, u, s;  // 16-column groups per workgroup, waves, K steps per stage, K slices
+};
+DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K);
+// Workspace bytes of the plan's split-K partials (0 without a split).
+size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K);
+
+// ws / ws_bytes: the split-K partials; a workspace smaller than
+// decode_workspace_bytes() runs the plan without a split.
+hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
+                              int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s);
 
 // NVFP4 x NVFP4 at decode shapes: M <= kSkinnyMaxM, K % 32 == 0, codes
 // 16-byte and scales 2-byte aligned (nvfp4_gemm checks and otherwise uses the
 // tile kernel).
 hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
-                               int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                               hipStream_t s);
+                               int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
+                               size_t ws_bytes, hipStream_t s);
 
 // Fused decode (BF16 activations quantized into LDS by every workgroup):
 // M <= 16, M * K <= kFusedDecodeMaxElems, K % 32 == 0, x rows 16-byte
 // aligned; dynamic != 0 computes alpha_A in every workgroup.
 hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, int dynamic,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
-                               int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                               hipStream_t s);
+                               int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
+                               size_t ws_bytes, hipStream_t s);
 
 // nvfp4_quant_gemm routes M <= kFusedDecodeMaxM with M * K <=
 // kFusedDecodeMaxElems (108 KB of codes and scales in LDS: every Qwen3-8B
 // layer at 16 tokens) to the fused decode kernel.
-constexpr int64_t kFusedDecodeMaxM = 16;
+constexpr int64_t kFusedDecodeMaxM = 2;
 constexpr int64_t kFusedDecodeMaxElems = 16 * 12288;
 
 // Largest M routed to the skinny decode kernels by bf16_gemm and nvfp4_gemm.

@@ -112,7 +112,37 @@ __global__ __launch_bounds__(kThreads) void alpha_kernel(const uint32_t *__restr
     if (threadIdx.x == 0) *alpha = a;
 }
 
-template <bool kDynamic>
+// Tensor-scale source of the quantize pass: static (the caller's alpha), the
+// amax pass's partials, or the workgroup's own pass over a small tensor.
+enum AlphaSrc { ALPHA_STATIC = 0, ALPHA_PARTIALS = 1, ALPHA_SELF = 2 };
+
+// Max |x| over a whole small tensor by one workgroup (FP32 bits of the BF16
+// maximum): every workgroup of the single-launch mode reads the tensor once
+// from L2 instead of waiting for a separate amax launch.
+__device__ __forceinline__ uint32_t tensor_amax_bits(const uint16_t *__restrict__ x, uint32_t rows, uint32_t octs,
+                                                     int64_t ld) {
+    ushort2_t m = {0, 0};
+    const uint32_t total = rows * octs;
+    for (uint32_t o0 = threadIdx.x; o0 < total; o0 += kThreads * 4) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t o = o0 + u * kThreads, r = o < total ? o / octs : 0u;
+            v[u] = o < total ? *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (o - r * octs) * 8)
+                             : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
+        }
+    }
+    return max((uint32_t)m.x, (uint32_t)m.y) << 16;
+}
+
+template <int kAlpha>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
                                                             uint8_t *__restrict__ scales, float *__restrict__ alpha_io,
@@ -145,21 +175,25 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     // loaded without branches; entries past nparts read as zero)
     constexpr int kPartsPerThread = kMaxParts / kThreads;
     uint32_t pv[kPartsPerThread];
-    if (kDynamic) {
+    if (kAlpha == ALPHA_PARTIALS) {
         const rsrc_t ps = make_rsrc(partials, (uint32_t)nparts * 4u);
 #pragma unroll
         for (int j = 0; j < kPartsPerThread; ++j)
             pv[j] = __builtin_amdgcn_raw_buffer_load_b32(ps, (threadIdx.x + j * kThreads) * 4u, 0, 0);
     }
-    const float alpha_in = kDynamic ? 0.0f : *alpha_io;
+    const float alpha_in = kAlpha == ALPHA_STATIC ? *alpha_io : 0.0f;
     asm volatile("" ::: "memory");
     uint4 va[2 * kBlk], vb[2 * kBlk];
     load_item(it, va);
     float alpha = alpha_in;
-    if (kDynamic) {
+    if (kAlpha != ALPHA_STATIC) {
         uint32_t pmax = 0;
+        if constexpr (kAlpha == ALPHA_PARTIALS) {
 #pragma unroll
-        for (int j = 0; j < kPartsPerThread; ++j) pmax = max(pmax, pv[j]);
+            for (int j = 0; j < kPartsPerThread; ++j) pmax = max(pmax, pv[j]);
+        } else {
+            pmax = tensor_amax_bits(x, (uint32_t)rows, octs, ld);
+        }
         alpha = alpha_from_max(pmax);
         if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_io = alpha;
     }
@@ -224,7 +258,7 @@ int64_t quant_items(int64_t rows, int64_t cols) { return rows * (((cols >> 3) + 
 // pipelined).
 // The per-device count is cached in an atomic: threads that race on the first
 // call compute the same value and store it, so no lock is needed.
-template <bool kDynamic>
+template <int kAlpha>
 int quant_grid(int64_t rows, int64_t cols) {
     static std::atomic<int> resident_cache[16];
     int dev = 0;
@@ -233,7 +267,7 @@ int quant_grid(int64_t rows, int64_t cols) {
     if (resident == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_kernel<kDynamic>, kThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_kernel<kAlpha>, kThreads, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 4;
@@ -287,17 +321,22 @@ hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, i
     return hipGetLastError();
 }
 
+bool quantize_self_amax(int64_t rows, int64_t cols) { return rows * cols <= kSelfAmaxMaxElems; }
+
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials, int nparts,
                            hipStream_t s) {
     if (quant_items(rows, cols) >= (int64_t(1) << 31) || cols >= (int64_t(1) << 30)) return hipErrorInvalidValue;
-    dim3 grid(dynamic ? quant_grid<true>(rows, cols) : quant_grid<false>(rows, cols)), block(kThreads);
-    if (dynamic)
-        hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, s, x, rows, cols, ld, codes, scales, alpha,
-                           partials, nparts);
+    const dim3 block(kThreads);
+    if (dynamic && quantize_self_amax(rows, cols))
+        hipLaunchKernelGGL(quantize_kernel<ALPHA_SELF>, dim3(quant_grid<ALPHA_SELF>(rows, cols)), block, 0, s, x, rows,
+                           cols, ld, codes, scales, alpha, partials, nparts);
+    else if (dynamic)
+        hipLaunchKernelGGL(quantize_kernel<ALPHA_PARTIALS>, dim3(quant_grid<ALPHA_PARTIALS>(rows, cols)), block, 0, s,
+                           x, rows, cols, ld, codes, scales, alpha, partials, nparts);
     else
-        hipLaunchKernelGGL(quantize_kernel<false>, grid, block, 0, s, x, rows, cols, ld, codes, scales, alpha,
-                           partials, nparts);
+        hipLaunchKernelGGL(quantize_kernel<ALPHA_STATIC>, dim3(quant_grid<ALPHA_STATIC>(rows, cols)), block, 0, s, x,
+                           rows, cols, ld, codes, scales, alpha, partials, nparts);
     return hipGetLastError();
 }
 

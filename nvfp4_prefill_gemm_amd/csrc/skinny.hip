@@ -2,18 +2,27 @@
 //
 // BF16: decode keeps the original BF16 weights (Mix-Quant Section 3.3,
 // "Prefill-Decode Disaggregation Deployment") and is bound by streaming W
-// from HBM: 2*N*K bytes against 2*M*N*K flops.  Each workgroup owns a strip
-// of NG*16 weight rows; its waves split K in 32-wide steps (interleaved, so
-// the waves of a workgroup read neighbouring 64-byte pieces of the same
-// rows), load through buffer resources over the valid rows (steps past K and
-// rows past N or M read zeros, so the loop has no branches), keep two
-// register stages of U steps in flight, and run 16x16x32 BF16 MFMAs with X
+// from HBM: 2*N*K bytes against 2*M*N*K flops.  A workgroup owns a strip of
+// NG*16 weight rows and one slice of K (grid: column strips x K slices); its
+// waves split the slice in 32-wide steps (interleaved, so the waves of a
+// workgroup read neighbouring 64-byte pieces of the same rows), load through
+// buffer resources over the valid rows (steps past the slice or K and rows
+// past N or M read zeros, so the loop has no branches), keep two register
+// stages of U steps in flight, and run 16x16x32 BF16 MFMAs with X
 // zero-padded to MG*16 rows.  The per-wave partial tiles are summed through
 // LDS at the end.
 //
+// Splitting K over workgroups: without it every workgroup of a narrow strip
+// streams the whole batch X, so at batch 32-64 the batch bytes crossing L2
+// exceed the weight bytes several times over.  With S slices a strip of
+// S times as many columns keeps the same number of workgroups, and each reads
+// only its slice of X.  Each workgroup then writes its FP32 partial tile to a
+// caller-provided workspace [S][M][N], and a second kernel sums the S
+// partials in slice order (deterministic) and applies the epilogue.
+//
 // NVFP4 (both operands E2M1 + E4M3 per 16, the uniform-NVFP4 and
-// FP4-decode variants of Mix-Quant's ablations, Section 4): the same split-K
-// layout streams 0.5625 bytes per weight instead of 2.  A lane's 16-byte code
+// FP4-decode variants of Mix-Quant's ablations, Section 4): the same layout
+// streams 0.5625 bytes per weight instead of 2.  A lane's 16-byte code
 // load covers 32 consecutive K; the four 16x16x32 MFMA sub-steps of a
 // 128-wide K chunk take its four 8-code words, so sub-step t of lane group g
 // holds K = 128c + 32g + 8t + i on both operands (the same permutation of K
@@ -22,13 +31,13 @@
 // the epilogue as in the prefill GEMM.
 //
 // Fused decode (nvfp4_quant_gemm with M * K <= 196608): the workgroup first
-// quantizes the BF16 batch itself, one 8-element group per thread with the
-// quantizer's own Eq. 3 / Eq. 2 functions, into LDS (a dynamic tensor scale
-// is formed from a first pass over the batch; every workgroup derives the
-// same alpha_A and workgroup 0 stores it), then runs the loop above with the
-// activation codes read from LDS.  Codes, scales and the summation order
-// equal those of quantize followed by the decode GEMM, so the two paths agree
-// bit for bit.
+// quantizes the part of the BF16 batch its K slice needs, one 8-element group
+// per thread with the quantizer's own Eq. 3 / Eq. 2 functions, into LDS (a
+// dynamic tensor scale is formed from a first pass over the whole batch;
+// every workgroup derives the same alpha_A and workgroup 0 stores it), then
+// runs the loop above with the activation codes read from LDS.  Codes, scales
+// and the summation order equal those of quantize followed by the decode GEMM
+// with the same slicing, so the two paths agree bit for bit.
 #include <stdlib.h>
 #include <string.h>
 
@@ -41,10 +50,15 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f4_t;
 
+// Epilogue of a decode workgroup: the final output (FP32 or BF16, y =
+// (sum * sa) * sw), or the raw FP32 partial of K slice blockIdx.y into the
+// workspace [S][M][N].
+enum DecOut { DOUT_F32 = 0, DOUT_BF16 = 1, DOUT_PARTIAL = 2 };
+
 // Sum the per-wave 16x16 partial tiles of a workgroup through LDS, one
-// (row group, column group) tile at a time, and store y = (sum * sa) * sw:
+// (row group, column group) tile at a time, and store them:
 // out[m = i*16 + (l>>4)*4 + r][n = n0 + j*16 + (l & 15)].
-template <int MG, int NG, int WAVES, bool kOutBf16>
+template <int MG, int NG, int WAVES, int kOut>
 __device__ __forceinline__ void tile_reduce(const f4_t (&acc)[MG][NG], float sa, float sw, int64_t M, int64_t N,
                                             int64_t n0, void *__restrict__ out, int64_t ld_out) {
     __shared__ float red[WAVES][64][4];
@@ -62,26 +76,37 @@ __device__ __forceinline__ void tile_reduce(const f4_t (&acc)[MG][NG], float sa,
                 float s = 0.f;
 #pragma unroll
                 for (int v = 0; v < WAVES; ++v) s += red[v][l][r];
-                const float y = (s * sa) * sw;
                 const int64_t m = i * 16 + (l >> 4) * 4 + r, n = n0 + j * 16 + (l & 15);
                 if (m < M && n < N) {
-                    if (kOutBf16)
-                        reinterpret_cast<uint16_t *>(out)[m * ld_out + n] = (uint16_t)f32_to_bf16_bits(y);
-                    else
-                        reinterpret_cast<float *>(out)[m * ld_out + n] = y;
+                    if constexpr (kOut == DOUT_PARTIAL) {
+                        reinterpret_cast<float *>(out)[((int64_t)blockIdx.y * M + m) * N + n] = s;
+                    } else {
+                        const float y = (s * sa) * sw;
+                        if constexpr (kOut == DOUT_BF16)
+                            reinterpret_cast<uint16_t *>(out)[m * ld_out + n] = (uint16_t)f32_to_bf16_bits(y);
+                        else
+                            reinterpret_cast<float *>(out)[m * ld_out + n] = y;
+                    }
                 }
             }
         }
 }
 
-template <int MG, int NG, int WAVES, int U, bool kOutBf16>
+// K steps [sb, se) of this workgroup's slice: slice blockIdx.y of `sps` steps.
+__device__ __forceinline__ void slice_steps(int64_t steps, int64_t sps, int64_t &sb, int64_t &se) {
+    sb = (int64_t)blockIdx.y * sps;
+    se = sb + sps < steps ? sb + sps : steps;
+}
+
+template <int MG, int NG, int WAVES, int U, int kOut>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                             int64_t M, int64_t N, int64_t K, void *__restrict__ out,
-                                                            int64_t ld_out) {
+                                                            int64_t ld_out, int64_t sps) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int kq = (lane >> 4) * 8;
-    const int64_t KS = (K + 31) >> 5;
+    int64_t sb, se;
+    slice_steps((K + 31) >> 5, sps, sb, se);
 
     f4_t acc[MG][NG];
 #pragma unroll
@@ -90,7 +115,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
         for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
     // buffer resources over this workgroup's weight rows and over X: rows past
-    // N or M and steps past K read zeros (offset beyond the resource)
+    // N or M and steps past the slice or K read zeros (offset beyond the resource)
     const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
     const rsrc_t wrs = make_rsrc(w + n0 * K, (uint32_t)(nrows * K * 2));
     const rsrc_t xrs = make_rsrc(x, (uint32_t)(M * K * 2));
@@ -108,8 +133,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
     auto load = [&](int64_t ks0, WStage &bw, XStage &ax) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t k = (ks0 + (int64_t)u * WAVES) * 32 + kq;
-            const bool kin = k + 8 <= K;  // also false past the last step
+            const int64_t ks = ks0 + (int64_t)u * WAVES, k = ks * 32 + kq;
+            const bool kin = ks < se && k + 8 <= K;
 #pragma unroll
             for (int j = 0; j < NG; ++j) bw[u][j] = buf_load16(wrs, kin ? wro[j] + (uint32_t)(k * 2) : kBufOOB);
 #pragma unroll
@@ -130,54 +155,42 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
     const int64_t stride = (int64_t)WAVES * U;
     WStage bw0, bw1;
     XStage ax0, ax1;
-    int64_t ks0 = wave;
+    int64_t ks0 = sb + wave;
     load(ks0, bw0, ax0);
     for (;;) {
         const int64_t k1 = ks0 + stride;
         load(k1, bw1, ax1);
         compute(bw0, ax0);
-        if (k1 >= KS) break;
+        if (k1 >= se) break;
         const int64_t k2 = k1 + stride;
         load(k2, bw0, ax0);
         compute(bw1, ax1);
-        if (k2 >= KS) break;
+        if (k2 >= se) break;
         ks0 = k2;
     }
 
-    tile_reduce<MG, NG, WAVES, kOutBf16>(acc, 1.0f, 1.0f, M, N, n0, out, ld_out);
+    tile_reduce<MG, NG, WAVES, kOut>(acc, 1.0f, 1.0f, M, N, n0, out, ld_out);
 }
 
-template <int MG, int NG, int WAVES, int U>
-hipError_t launch_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out, int out_type,
-                      int64_t ld_out, hipStream_t s) {
-    const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
-    if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (out_type == OUT_BF16)
-        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, true>), dim3((unsigned)nb), dim3(WAVES * 64), 0, s, a, w,
-                           M, N, K, out, ld_out);
-    else
-        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, false>), dim3((unsigned)nb), dim3(WAVES * 64), 0, s, a, w,
-                           M, N, K, out, ld_out);
-    return hipGetLastError();
-}
-
-// Source of the A operand of the decode kernel.
+// Source of the A operand of the NVFP4 decode kernel.
 enum ASrc { A_NVFP4 = 0, A_BF16_DYNAMIC = 1, A_BF16_STATIC = 2 };
 
 // NVFP4 x NVFP4, M <= MG*16, NG*16 weight rows per workgroup, K % 32 == 0,
 // 16-byte aligned codes and 4-byte aligned scales.  kA != A_NVFP4: A is
 // BF16 [M, ld_x] (16-byte aligned rows, MG == 1), quantized into LDS
-// (M * K * 9 / 16 bytes of dynamic shared memory).
-template <int MG, int NG, int WAVES, int U, bool kOutBf16, int kA = A_NVFP4>
+// (M * K * 9 / 16 bytes of dynamic shared memory; the slice's part is filled).
+template <int MG, int NG, int WAVES, int U, int kOut, int kA = A_NVFP4>
 __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, float *__restrict__ a_alpha,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, const float *__restrict__ w_alpha, int64_t M,
-    int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out, const uint16_t *__restrict__ x, int64_t ld_x) {
+    int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out, const uint16_t *__restrict__ x, int64_t ld_x,
+    int64_t sps) {
     static_assert(kA == A_NVFP4 || MG == 1, "BF16 activations: one 16-row group");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int64_t cb = K >> 1, sb = K >> 4;  // code and scale bytes per row
-    const int64_t KC = (K + 127) >> 7;       // 128-wide K chunks
+    int64_t cs, ce;                          // this slice's 128-wide K chunks [cs, ce)
+    slice_steps((K + 127) >> 7, sps, cs, ce);
     const int kg = (lane >> 4) * 32;         // this lane group's K offset in a chunk
 
     f4_t acc[MG][NG];
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
     // buffer resources over this workgroup's weight rows (and over A in global
-    // memory): rows past N or M and chunks past K read zeros
+    // memory): rows past N or M and chunks past the slice or K read zeros
     const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
     const rsrc_t wcs = make_rsrc(wc + n0 * cb, (uint32_t)(nrows * cb));
     const rsrc_t wss = make_rsrc(ws + n0 * sb, (uint32_t)(nrows * sb));
@@ -220,8 +233,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     auto load_part = [&](int64_t c0, NStage &st, bool do_w, bool do_x) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t k = (c0 + (int64_t)u * WAVES) * 128 + kg;
-            const bool kin = k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
+            const int64_t c = c0 + (int64_t)u * WAVES, k = c * 128 + kg;
+            const bool kin = c < ce && k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
             const uint32_t kc = (uint32_t)(k >> 1), ksc = (uint32_t)(k >> 4);
             if (do_w) {
 #pragma unroll
@@ -272,28 +285,26 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             }
     };
     NStage s0, s1;
-    if constexpr (kA != A_NVFP4) load_part(wave, s0, true, false);
+    if constexpr (kA != A_NVFP4) load_part(cs + wave, s0, true, false);
     if constexpr (kA != A_NVFP4) {
-        // quantize the whole batch into LDS: codes [M][K/2], then scales [M][K/16]
+        // quantize the slice's part of the batch into LDS: codes [M][K/2],
+        // then scales [M][K/16]
         extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
         uint8_t *lcw = xlds, *lsw = xlds + M * cb;
         // 32-bit indexing: M * K <= kFusedDecodeMaxElems
-        const uint32_t octs = (uint32_t)(K >> 3), total = (uint32_t)M * octs;  // total is even (K % 32 == 0)
-        auto load_oct = [&](uint32_t o) __attribute__((always_inline)) {
-            if (o >= total) return make_uint4(0, 0, 0, 0);
-            const uint32_t r = o / octs;
-            return *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld_x + (o - r * octs) * 8);
+        const uint32_t octs = (uint32_t)(K >> 3), total = (uint32_t)M * octs;
+        auto load_oct = [&](uint32_t r, uint32_t oc) __attribute__((always_inline)) {
+            return *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld_x + oc * 8);
         };
-        if constexpr (kA == A_BF16_STATIC) {
-            alpha_a = *a_alpha;
-        } else {
+        auto oct_amax = [](const uint4 &v) __attribute__((always_inline)) {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
             uint32_t am = 0;
-            for (uint32_t o = threadIdx.x; o < total; o += WAVES * 64) {
-                const uint4 v = load_oct(o);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
-            }
+            for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
+            return am;
+        };
+        // alpha from this thread's partial amax (workgroup-wide reduction)
+        auto set_alpha = [&](uint32_t am) __attribute__((always_inline)) {
             for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
             __shared__ uint32_t wmax[WAVES];
             if (lane == 0) wmax[wave] = am;
@@ -302,29 +313,75 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
 #pragma unroll
             for (int v = 1; v < WAVES; ++v) t = max(t, wmax[v]);
             alpha_a = div_rn(bf16_bits_to_f32(t), kAlphaDen);
-            if (blockIdx.x == 0 && threadIdx.x == 0) *a_alpha = alpha_a;
-        }
+            if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a_alpha = alpha_a;
+        };
         // Eq. 3 against t = alpha * 6 (one reciprocal per workgroup), Eq. 2 by
-        // quant8_fast, or quant8 for a block outside its range
-        const float at = alpha_a * kQmax, art = at > 0.0f ? div_rn(1.0f, at) : 0.0f;
-        // thread pairs (t, t ^ 1) hold the two halves of a 16-element block
-        for (uint32_t base = 0; base < total; base += WAVES * 64) {
-            const uint32_t o = base + threadIdx.x;
-            const uint4 v = load_oct(o);
+        // quant8_fast, or quant8 for a block outside its range, for octet oc
+        // of row r held in v; thread pairs (t, t ^ 1) hold the two halves of
+        // a 16-element block (every call site keeps octet parity = lane
+        // parity), and `valid` is uniform across each pair.
+        float at = 0.0f, art = 0.0f;
+        auto quant_oct = [&](const uint4 &v, bool valid, uint32_t r, uint32_t oc) __attribute__((always_inline)) {
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-            uint32_t am = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) am = max(am, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
+            const uint32_t am = oct_amax(v);
             const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false);
             const float amax_b = bf16_bits_to_f32(max(am, other));
             const uint32_t code = e4m3_encode(at > 0.0f ? div_rn_recip(amax_b, at, art) : 0.0f);
             const float d = alpha_a * e4m3_decode(code);
             const bool fast = d >= 0x1p-90f && d <= 0x1p100f && amax_b <= d * 0x1p120f;
             const uint32_t q = fast ? quant8_fast(w4, d, div_rn(1.0f, d)) : quant8(w4, d);
-            if (o < total) {
-                const uint32_t r = o / octs, oc = o - r * octs;
+            if (valid) {
                 *reinterpret_cast<uint32_t *>(lcw + r * cb + oc * 4) = q;
                 if ((oc & 1) == 0) lsw[r * sb + (oc >> 1)] = (uint8_t)code;
+            }
+        };
+        constexpr uint32_t NT = WAVES * 64, kRegOcts = 4;
+        const bool whole = cs == 0 && (uint32_t)ce * 16u >= octs;
+        if (whole && total <= kRegOcts * NT) {
+            // the batch fits in registers (up to four octets per thread): one
+            // load, the amax, then quantization from the same registers
+            uint4 v[kRegOcts];
+#pragma unroll
+            for (uint32_t i = 0; i < kRegOcts; ++i) {
+                const uint32_t o = threadIdx.x + i * NT, r = o < total ? o / octs : 0u;
+                v[i] = o < total ? load_oct(r, o - r * octs) : make_uint4(0, 0, 0, 0);
+            }
+            if constexpr (kA == A_BF16_STATIC) {
+                alpha_a = *a_alpha;
+            } else {
+                uint32_t am = 0;
+#pragma unroll
+                for (uint32_t i = 0; i < kRegOcts; ++i) am = max(am, oct_amax(v[i]));
+                set_alpha(am);
+            }
+            at = alpha_a * kQmax;
+            art = at > 0.0f ? div_rn(1.0f, at) : 0.0f;
+#pragma unroll
+            for (uint32_t i = 0; i < kRegOcts; ++i) {
+                const uint32_t o = threadIdx.x + i * NT, r = o < total ? o / octs : 0u;
+                if (i * NT < total) quant_oct(v[i], o < total, r, o - r * octs);  // wave-uniform condition
+            }
+        } else {
+            if constexpr (kA == A_BF16_STATIC) {
+                alpha_a = *a_alpha;
+            } else {  // dynamic: the amax of the whole batch
+                uint32_t am = 0;
+                for (uint32_t o = threadIdx.x; o < total; o += NT) {
+                    const uint32_t r = o / octs;
+                    am = max(am, oct_amax(load_oct(r, o - r * octs)));
+                }
+                set_alpha(am);
+            }
+            at = alpha_a * kQmax;
+            art = at > 0.0f ? div_rn(1.0f, at) : 0.0f;
+            // the slice's octets of each row are [o0, o1); their count per row
+            // is a multiple of 4 (K % 32 == 0), so pairs never straddle rows
+            const uint32_t o0 = (uint32_t)cs * 16u, o1 = min((uint32_t)ce * 16u, octs), so = o1 - o0;
+            const uint32_t stotal = (uint32_t)M * so;
+            for (uint32_t base = 0; base < stotal; base += NT) {
+                const uint32_t o = base + threadIdx.x;
+                const uint32_t r = o < stotal ? o / so : 0u, oc = o < stotal ? o0 + (o - r * so) : 0u;
+                quant_oct(o < stotal ? load_oct(r, oc) : make_uint4(0, 0, 0, 0), o < stotal, r, oc);
             }
         }
         __syncthreads();
@@ -333,46 +390,127 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     }
 
     const int64_t stride = (int64_t)WAVES * U;
-    int64_t c0 = wave;
+    int64_t c0 = cs + wave;
     if constexpr (kA != A_NVFP4) load_part(c0, s0, false, true);  // the weights are in flight already
     else load(c0, s0);
     for (;;) {
         const int64_t c1 = c0 + stride;
         load(c1, s1);
         compute(s0);
-        if (c1 >= KC) break;
+        if (c1 >= ce) break;
         const int64_t c2 = c1 + stride;
         load(c2, s0);
         compute(s1);
-        if (c2 >= KC) break;
+        if (c2 >= ce) break;
         c0 = c2;
     }
 
-    tile_reduce<MG, NG, WAVES, kOutBf16>(acc, kA == A_NVFP4 ? *a_alpha : alpha_a, *w_alpha, M, N, n0, out, ld_out);
+    float sa = 1.0f, sw = 1.0f;
+    if constexpr (kOut != DOUT_PARTIAL) {
+        sa = kA == A_NVFP4 ? *a_alpha : alpha_a;
+        sw = *w_alpha;
+    }
+    tile_reduce<MG, NG, WAVES, kOut>(acc, sa, sw, M, N, n0, out, ld_out);
 }
 
+// Sum of the S partial tiles in slice order, then the epilogue
+// y = (sum * alpha_A) * alpha_W (alphas absent: 1) into out [M, ld_out].
+template <bool kOutBf16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int S, int64_t M,
+                                                            int64_t N, const float *__restrict__ a_alpha,
+                                                            const float *__restrict__ w_alpha, void *__restrict__ out,
+                                                            int64_t ld_out) {
+    const int64_t mn = M * N;
+    const float sa = a_alpha ? *a_alpha : 1.0f, sw = w_alpha ? *w_alpha : 1.0f;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += (int64_t)gridDim.x * 256) {
+        float s = part[i];
+        for (int j = 1; j < S; ++j) s += part[(int64_t)j * mn + i];
+        const float y = (s * sa) * sw;
+        const int64_t m = i / N, n = i - m * N;
+        if (kOutBf16)
+            reinterpret_cast<uint16_t *>(out)[m * ld_out + n] = (uint16_t)f32_to_bf16_bits(y);
+        else
+            reinterpret_cast<float *>(out)[m * ld_out + n] = y;
+    }
+}
+
+hipError_t launch_reduce(const float *part, int S, int64_t M, int64_t N, const float *a_alpha, const float *w_alpha,
+                         void *out, int out_type, int64_t ld_out, hipStream_t s) {
+    const int64_t mn = M * N;
+    int64_t g = (mn + 255) / 256;
+    if (g > 4096) g = 4096;
+    if (out_type == OUT_BF16)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)g), dim3(256), 0, s, part, S, M, N, a_alpha,
+                           w_alpha, out, ld_out);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)g), dim3(256), 0, s, part, S, M, N, a_alpha,
+                           w_alpha, out, ld_out);
+    return hipGetLastError();
+}
+
+// Steps per slice for S slices of `steps` steps (S > 1 only while every
+// slice keeps at least one step).
+int64_t steps_per_slice(int64_t steps, int S) { return S <= 1 ? (steps > 0 ? steps : 1) : (steps + S - 1) / S; }
+
+// BF16 decode kernel with NG column groups, WAVES waves, U steps per stage,
+// S slices of K (S > 1: partials into `part`, then the reduction kernel).
+template <int MG, int NG, int WAVES, int U>
+hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
+                           int out_type, int64_t ld_out, int S, float *part, hipStream_t s) {
+    const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
+    if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t sps = steps_per_slice((K + 31) >> 5, S);
+    const int ns = S > 1 ? (int)((((K + 31) >> 5) + sps - 1) / sps) : 1;
+    const dim3 grid((unsigned)nb, (unsigned)ns), block(WAVES * 64);
+    if (ns > 1) {
+        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_PARTIAL>), grid, block, 0, s, a, w, M, N, K,
+                           (void *)part, N, sps);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        return launch_reduce(part, ns, M, N, nullptr, nullptr, out, out_type, ld_out, s);
+    }
+    if (out_type == OUT_BF16)
+        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_BF16>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
+                           sps);
+    else
+        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_F32>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
+                           sps);
+    return hipGetLastError();
+}
+
+// NVFP4 decode kernel (kA: NVFP4 activations, or BF16 ones quantized inside).
 template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4>
 hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
                             const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                            hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0) {
+                            int S, float *part, hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0) {
     const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t chunks = (K + 127) >> 7, sps = steps_per_slice(chunks, S);
+    const int ns = S > 1 ? (int)((chunks + sps - 1) / sps) : 1;
     const size_t lds = kA == A_NVFP4 ? 0 : (size_t)(M * K / 2 + M * K / 16);
+    const int kind = ns > 1 ? DOUT_PARTIAL : out_type == OUT_BF16 ? DOUT_BF16 : DOUT_F32;
+    const void *f = kind == DOUT_PARTIAL ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA>
+                    : kind == DOUT_BF16  ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA>
+                                         : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA>;
     if (kA != A_NVFP4) {
-        static std::atomic<uint32_t> attr_done[2];
-        const int o = out_type == OUT_BF16;
-        const void *f = o ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>
-                          : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, false, kA>;
-        if (hipError_t e = set_dyn_lds_once(attr_done[o], f, (int)(kFusedDecodeMaxElems * 9 / 16)); e != hipSuccess)
+        static std::atomic<uint32_t> attr_done[3];
+        if (hipError_t e = set_dyn_lds_once(attr_done[kind], f, (int)(kFusedDecodeMaxElems * 9 / 16)); e != hipSuccess)
             return e;
     }
-    if (out_type == OUT_BF16)
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, true, kA>), dim3((unsigned)nb), dim3(WAVES * 64),
-                           lds, s, ac, as, aa, wc, ws, wa, M, N, K, out, ld_out, x, ld_x);
+    const dim3 grid((unsigned)nb, (unsigned)ns), block(WAVES * 64);
+    void *dst = ns > 1 ? (void *)part : out;
+    const int64_t ld = ns > 1 ? N : ld_out;
+    if (kind == DOUT_PARTIAL)
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA>), grid, block, lds, s, ac, as, aa,
+                           wc, ws, wa, M, N, K, dst, ld, x, ld_x, sps);
+    else if (kind == DOUT_BF16)
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA>), grid, block, lds, s, ac, as, aa, wc,
+                           ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     else
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, false, kA>), dim3((unsigned)nb), dim3(WAVES * 64),
-                           lds, s, ac, as, aa, wc, ws, wa, M, N, K, out, ld_out, x, ld_x);
-    return hipGetLastError();
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA>), grid, block, lds, s, ac, as, aa, wc,
+                           ws, wa, M, N, K, dst, ld, x, ld_x, sps);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (ns > 1) return launch_reduce(part, ns, M, N, aa, wa, out, out_type, ld_out, s);
+    return hipSuccess;
 }
 
 __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
@@ -382,118 +520,117 @@ __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, 
 
 }  // namespace
 
-// NVFP4_SKINNY_CFG=8|16 overrides the waves per workgroup of the BF16 decode
-// kernel with one column group (tuning knob; default 16).
-int skinny_cfg() {
-    static const int v = [] {  // read once; thread-safe initialisation
-        const char *e = getenv("NVFP4_SKINNY_CFG");
-        return (e && !strcmp(e, "8")) ? 1 : 0;
-    }();
-    return v;
+// Decode plan: column groups per workgroup (ng), waves per workgroup, K steps
+// per register stage (u) and K slices (s), from a sweep of every
+// configuration over the Qwen3-8B projections at batch 1-64 (graph replay,
+// rotated weights).  Batches up to 16 are fastest unsplit; larger ones split
+// K so that narrow layers still give about 256 workgroups of wide strips
+// (BF16), or, for NVFP4 whose weights are 3.6x smaller, only on long K.
+DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
+    if (kind == DECODE_BF16) {
+        if (M <= 4) return {1, 16, 1, 1};
+        if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1};
+        const int ng = N >= 6144 || M > 32 ? 4 : 2;
+        const int64_t nb = (N + 16 * ng - 1) / (16 * ng);
+        const int s = nb <= 64 ? 4 : 2;
+        return ng == 4 ? DecodePlan{4, 4, 2, s} : DecodePlan{2, 8, 1, s};
+    }
+    // NVFP4 and fused: the same plan, so both sum in the same order
+    if (M <= 16) return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 16, 1, 1};
+    if (K >= 8192) return {4, 8, 1, 4};
+    if (N >= 16384 && M > 32) return {4, 8, 1, 1};
+    return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 8, 2, 1};
 }
 
-// K-steps per register stage.  With one row group a single step per stage
-// (two steps in flight per wave) measured fastest on the Qwen3-8B decode
-// layers; more row groups take two.
+size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
+    const DecodePlan p = decode_plan(kind, M, N, K);
+    return p.s > 1 ? (size_t)p.s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+namespace {
+
+// the plan's slice count when the workspace holds its partials, else 1
+int plan_slices(const DecodePlan &p, int64_t M, int64_t N, void *ws, size_t ws_bytes) {
+    const size_t need = (size_t)p.s * (size_t)M * (size_t)N * sizeof(float);
+    return p.s > 1 && ws && ws_bytes >= need ? p.s : 1;
+}
+
 template <int MG>
-constexpr int skinny_u() { return MG == 1 ? 1 : 2; }
-
-template <int MG, int NG>
-hipError_t launch_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out, int out_type,
-                     int64_t ld_out, hipStream_t s) {
-    if (skinny_cfg() == 1) return launch_cfg<MG, NG, 8, skinny_u<MG>()>(a, w, M, N, K, out, out_type, ld_out, s);
-    return launch_cfg<MG, NG, 16, skinny_u<MG>()>(a, w, M, N, K, out, out_type, ld_out, s);
+hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
+                          int out_type, int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s) {
+    if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
+    if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
+    if (p.ng == 2) return launch_bf16_cfg<MG, 2, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
+    return launch_bf16_cfg<MG, 1, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
 }
 
-// NVFP4_DECODE_NG=1|2|4 forces the number of 16-column groups per
-// workgroup (tuning knob); by default it follows the layer width below.
-int decode_ng_knob() {
-    static const int v = [] {  // read once; thread-safe initialisation
-        const char *e = getenv("NVFP4_DECODE_NG");
-        const int n = e ? atoi(e) : 0;
-        return n == 1 || n == 2 || n == 4 ? n : 0;
-    }();
-    return v;
-}
-
-// With several 16-row groups of X, each X fragment a wave loads is reused
-// across NG weight-row groups; wide layers (N >= 6144 here: >= 192 workgroups
-// of 32 columns) take NG = 2 and 8 waves, very wide ones (N >= 16384) NG = 4,
-// narrow ones keep one group so every CU still gets a workgroup.
 template <int MG>
-hipError_t launch_mg_ng(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
-                        int out_type, int64_t ld_out, hipStream_t s) {
-    int ng = decode_ng_knob();
-    if (ng == 0) ng = MG == 1 ? 1 : N >= 16384 ? 4 : N >= 6144 ? 2 : 1;
-    if (ng == 4) return launch_cfg<MG, 4, 8, 2>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (ng == 2) return launch_cfg<MG, 2, 8, 2>(a, w, M, N, K, out, out_type, ld_out, s);
-    return launch_mg<MG, 1>(a, w, M, N, K, out, out_type, ld_out, s);
+hipError_t launch_nv_mg(const uint8_t *ac, const uint8_t *as, const float *aa_in, const uint8_t *wc,
+                        const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type,
+                        int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s) {
+    float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
+    if (p.ng == 4) return launch_nvfp4_cfg<MG, 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+    if (p.ng == 2) return launch_nvfp4_cfg<MG, 2, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+    if (p.waves == 8)
+        return launch_nvfp4_cfg<MG, 1, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+    return launch_nvfp4_cfg<MG, 1, 16, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
 }
+
+template <int kA>
+hipError_t launch_fused_a(const uint16_t *x, int64_t ld_x, float *a_alpha, const uint8_t *wc, const uint8_t *ws,
+                          const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                          const DecodePlan &p, int S, float *part, hipStream_t s) {
+    if (p.ng == 2)
+        return launch_nvfp4_cfg<1, 2, 8, 1, kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, S,
+                                                part, s, x, ld_x);
+    return launch_nvfp4_cfg<1, 1, 16, 1, kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, S,
+                                             part, s, x, ld_x);
+}
+
+}  // namespace
 
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
-                              int out_type, int64_t ld_out, hipStream_t s) {
-    if (M <= 16) return launch_mg_ng<1>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (M <= 32) return launch_mg_ng<2>(a, w, M, N, K, out, out_type, ld_out, s);
-    if (M <= 64) return launch_mg_ng<4>(a, w, M, N, K, out, out_type, ld_out, s);
+                              int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s) {
+    const DecodePlan p = decode_plan(DECODE_BF16, M, N, K);
+    const int S = plan_slices(p, M, N, ws, ws_bytes);
+    float *part = (float *)ws;
+    if (M <= 16) return launch_bf16_mg<1>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s);
+    if (M <= 32) return launch_bf16_mg<2>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s);
+    if (M <= 64) return launch_bf16_mg<4>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s);
     return hipErrorInvalidValue;
-}
-
-template <int MG>
-hipError_t launch_nv_ng(const uint8_t *ac, const uint8_t *as, const float *aa_in, const uint8_t *wc,
-                        const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type,
-                        int64_t ld_out, hipStream_t s) {
-    float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
-    int ng = decode_ng_knob();
-    // two 16-row weight groups per workgroup on wide layers (each X fragment
-    // then serves both): measured faster from N = 6144 at one and four row
-    // groups, slower at N = 4096; four groups were slower everywhere
-    if (ng == 0) ng = (MG == 1 || MG == 4) && N >= 6144 ? 2 : 1;
-    if (MG == 4 && ng == 4) ng = 2;  // four row groups by four column groups exceed the register file
-    constexpr int U = MG == 1 ? 2 : 1;  // chunks per register stage
-    switch (ng) {
-        case 2: return launch_nvfp4_cfg<MG, 2, 8, U>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
-        case 4: return launch_nvfp4_cfg<MG, MG == 4 ? 2 : 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
-        default: return launch_nvfp4_cfg<MG, 1, 16, U>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, s);
-    }
 }
 
 hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
-                               int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, hipStream_t s) {
+                               int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
+                               size_t ws_bytes, hipStream_t s) {
+    const DecodePlan p = decode_plan(DECODE_NVFP4, M, N, K);
+    const int S = plan_slices(p, M, N, ws, ws_bytes);
+    float *part = (float *)ws;
     if (M <= 16)
-        return launch_nv_ng<1>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
+        return launch_nv_mg<1>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
+                               p, S, part, s);
     if (M <= 32)
-        return launch_nv_ng<2>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
+        return launch_nv_mg<2>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
+                               p, S, part, s);
     if (M <= 64)
-        return launch_nv_ng<4>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out, s);
+        return launch_nv_mg<4>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
+                               p, S, part, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, int dynamic, const uint8_t *w_codes,
                                const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K,
-                               void *out, int out_type, int64_t ld_out, hipStream_t s) {
+                               void *out, int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s) {
     if (M > 16 || M * K > kFusedDecodeMaxElems) return hipErrorInvalidValue;
-    // wide layers: several 16-row weight groups per workgroup, so fewer
-    // workgroups quantize the batch (every one of them does)
-    const int ng = N >= 16384 ? 4 : N >= 6144 ? 2 : 1;
-    if (dynamic) {
-        if (ng == 4)
-            return launch_nvfp4_cfg<1, 4, 8, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha,
-                                                                M, N, K, out, out_type, ld_out, s, x, ld_x);
-        if (ng == 2)
-            return launch_nvfp4_cfg<1, 2, 8, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha,
-                                                                M, N, K, out, out_type, ld_out, s, x, ld_x);
-        return launch_nvfp4_cfg<1, 1, 16, 1, A_BF16_DYNAMIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M,
-                                                             N, K, out, out_type, ld_out, s, x, ld_x);
-    }
-    if (ng == 4)
-        return launch_nvfp4_cfg<1, 4, 8, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
-                                                           K, out, out_type, ld_out, s, x, ld_x);
-    if (ng == 2)
-        return launch_nvfp4_cfg<1, 2, 8, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
-                                                           K, out, out_type, ld_out, s, x, ld_x);
-    return launch_nvfp4_cfg<1, 1, 16, 1, A_BF16_STATIC>(nullptr, nullptr, a_alpha, w_codes, w_scales, w_alpha, M, N,
-                                                        K, out, out_type, ld_out, s, x, ld_x);
+    const DecodePlan p = decode_plan(DECODE_FUSED, M, N, K);
+    const int S = plan_slices(p, M, N, ws, ws_bytes);
+    float *part = (float *)ws;
+    if (dynamic)
+        return launch_fused_a<A_BF16_DYNAMIC>(x, ld_x, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type,
+                                              ld_out, p, S, part, s);
+    return launch_fused_a<A_BF16_STATIC>(x, ld_x, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
+                                         p, S, part, s);
 }
 
 hipError_t launch_fill_zero(void *out, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s) {

@@ -32,7 +32,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_quant_gemm", "bf16_gemm", "nvfp4_last_error",
-              "nvfp4_abi_version", "nvfp4_quantize_workspace_size", "nvfp4_quant_gemm_workspace_size"):
+              "nvfp4_abi_version", "nvfp4_quantize_workspace_size", "nvfp4_quant_gemm_workspace_size",
+              "nvfp4_gemm_workspace_size", "bf16_gemm_workspace_size", "nvfp4_quantize_noalloc"):
         assert n in names
 
 
@@ -42,14 +43,26 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.nvfp4_abi_version() == 1
+    assert L.nvfp4_abi_version() == 2
 
 
 def test_workspace_sizes(L):
     assert L.nvfp4_quantize_workspace_size(0, 4096) == 0
     assert L.nvfp4_quantize_workspace_size(8192, 4096) > 0
     assert L.nvfp4_quantize_workspace_size(8192, 4096) <= 4096
-    assert L.nvfp4_quant_gemm_workspace_size(128, 256) == L.nvfp4_quantize_workspace_size(128, 256)
+    # quantize into the workspace, then the GEMM: codes + scales + amax partials (256-byte aligned parts)
+    q = L.nvfp4_quant_gemm_workspace_size(128, 512, 256)
+    assert q >= 128 * 256 // 2 + 128 * 256 // 16 + L.nvfp4_quantize_workspace_size(128, 256)
+    # decode batches: at least the dynamic alpha's partials
+    assert L.nvfp4_quant_gemm_workspace_size(8, 4096, 4096) >= L.nvfp4_quantize_workspace_size(8, 4096)
+    # tile-kernel shapes need no GEMM workspace; decode shapes may (split K)
+    assert L.nvfp4_gemm_workspace_size(8192, 4096, 4096) == 0
+    assert L.bf16_gemm_workspace_size(8192, 4096, 4096) == 0
+    assert L.nvfp4_gemm_workspace_size(0, 4096, 4096) == 0
+    for f in (L.nvfp4_gemm_workspace_size, L.bf16_gemm_workspace_size):
+        for M in (1, 8, 64):
+            ws = f(M, 4096, 4096)
+            assert ws == 0 or ws % (M * 4096 * 4) == 0  # S slices of FP32 [M, N]
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -79,12 +92,12 @@ def test_gemm_argument_errors(L):
     from nvfp4_prefill_gemm_amd.binding import NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_OK
 
     g = L.nvfp4_gemm
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 24, FAKE, 0, 8, None) == NVFP4_EINVAL  # K % 16
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 5, 8, None) == NVFP4_EINVAL  # dtype
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 4, None) == NVFP4_EINVAL  # ld_out
-    assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL  # null alpha
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL
-    assert g(None, None, None, None, None, None, 0, 8, 32, None, 0, 8, None) == NVFP4_OK
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 24, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL  # K % 16
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 5, 8, None, 0, None) == NVFP4_EINVAL  # dtype
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 4, None, 0, None) == NVFP4_EINVAL  # ld_out
+    assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL  # null alpha
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 32, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL
+    assert g(None, None, None, None, None, None, 0, 8, 32, None, 0, 8, None, 0, None) == NVFP4_OK
     q = L.nvfp4_gemm_quant_out
     assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 24, 32, FAKE, FAKE, FAKE, None) == NVFP4_EINVAL  # N % 16
     assert b"multiple of 16" in L.nvfp4_last_error()
@@ -92,14 +105,18 @@ def test_gemm_argument_errors(L):
     assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 32, ctypes.c_void_p(0x1002), FAKE, FAKE, None) == NVFP4_EINVAL
     assert q(None, None, None, None, None, None, 0, 16, 32, None, None, None, None) == NVFP4_OK
     odd = ctypes.c_void_p(0x1002)
-    assert g(FAKE, odd, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None) == NVFP4_EINVAL  # scale align
+    assert g(FAKE, odd, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL  # scale align
     assert b"4-byte aligned" in L.nvfp4_last_error()
     b = L.bf16_gemm
-    assert b(FAKE, FAKE, 8, 8, 12, FAKE, 0, 8, None) == NVFP4_EUNSUPPORTED  # K % 8
-    assert b(None, FAKE, 8, 8, 16, FAKE, 0, 8, None) == NVFP4_EINVAL
+    assert b(FAKE, FAKE, 8, 8, 12, FAKE, 0, 8, None, 0, None) == NVFP4_EUNSUPPORTED  # K % 8
+    assert b(None, FAKE, 8, 8, 16, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL
     f = L.nvfp4_quant_gemm
     assert f(FAKE, 32, FAKE, 0, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None, 0, None) == -4  # workspace
     assert f(FAKE, 16, FAKE, 1, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, None, 0, None) == NVFP4_EINVAL  # ld_x
-    misaligned = ctypes.c_void_p(0x1002)  # dynamic alpha stores uint32 partials in the workspace
+    misaligned = ctypes.c_void_p(0x1008)  # workspaces hold uint32 / float partials and 16-byte code rows
     assert f(FAKE, 32, FAKE, 0, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, misaligned, 4096, None) == NVFP4_EINVAL
-    assert b"workspace is misaligned" in L.nvfp4_last_error()
+    assert b"workspace must be 16-byte aligned" in L.nvfp4_last_error()
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 32, FAKE, 0, 8, misaligned, 4096, None) == NVFP4_EINVAL
+    assert b"workspace must be 16-byte aligned" in L.nvfp4_last_error()
+    assert b(FAKE, FAKE, 8, 8, 16, FAKE, 0, 8, misaligned, 4096, None) == NVFP4_EINVAL
+    assert b"workspace must be 16-byte aligned" in L.nvfp4_last_error()

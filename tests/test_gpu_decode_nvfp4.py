@@ -115,12 +115,15 @@ def test_decode_kernel_agrees_with_tile_kernel(nv, oracle_mod):
 
 @pytest.mark.parametrize("M,N,K,ld_pad", [(1, 6144, 4096, 0), (1, 4096, 12288, 0), (2, 300, 4128, 8),
                                           (8, 24576, 4096, 0), (13, 17, 96, 24), (16, 1000, 1056, 0),
-                                          (16, 64, 12288, 0), (1, 520, 65536, 0),
-                                          # two and four 16-row weight groups per workgroup, last one partial
-                                          (3, 6200, 1056, 0), (1, 16400, 512, 8)])
+                                          (16, 64, 12288, 0), (1, 520, 65536, 0), (2, 64, 98304, 0),
+                                          (2, 24576, 4096, 16),
+                                          # two 16-row weight groups per workgroup, the last one partial
+                                          (3, 6200, 1056, 0), (1, 16400, 512, 8), (2, 6200, 12288, 0)])
 def test_fused_decode_equals_quantize_then_gemm(nv, oracle_mod, M, N, K, ld_pad):
-    """nvfp4_quant_gemm with M <= 16 and M * K <= 196608 quantizes the batch
-    inside the decode kernel: alpha, and the output in FP32 and BF16, equal
+    """nvfp4_quant_gemm at decode sizes: M <= 2 with M * K <= 196608
+    quantizes the batch inside the decode kernel (the batch held in registers
+    when it fits, else read twice), larger batches quantize once into the
+    workspace.  Either way alpha, and the output in FP32 and BF16, equal
     nvfp4_quantize followed by nvfp4_gemm bit for bit (dynamic and static
     alpha, strided x, the size limit itself); both within the gate of the
     oracle's exact product."""
@@ -171,8 +174,10 @@ def test_fused_decode_zero_batch_and_zero_rows(nv, oracle_mod):
 
 
 def test_fused_past_decode_limit_within_gate(nv, oracle_mod):
-    """M <= 16 with M * K > 196608 takes the tile fused kernel; it agrees with
-    the oracle (the unfused decode kernel sums in another order)."""
+    """M <= 16 with M * K > 196608: with its full workspace nvfp4_quant_gemm
+    quantizes into it and runs the decode GEMM (equal to quantize + gemm bit
+    for bit); with only the amax partials the tile kernel quantizes in its
+    staging and sums in another order.  Both within the gate."""
     import torch
 
     M, N, K = 16, 96, 12320
@@ -180,8 +185,51 @@ def test_fused_past_decode_limit_within_gate(nv, oracle_mod):
     a = wl.activations(M, K, g)
     wt = wl.weights(N, K, g)
     A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    wc, wsc, wal = u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]])
+    x = bf16_dev(a)
+    ref = oracle_mod.gemm_exact(*A, *W)
     say("fused past decode limit", M, N, K)
-    y, alpha = nv.nvfp4_quant_gemm(bf16_dev(a), u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]]),
-                                   out_dtype=torch.float32)
+    y, alpha = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=torch.float32)
     assert host(alpha)[0] == A[2]
-    parity.assert_gemm_close(host(y), oracle_mod.gemm_exact(*A, *W), parity.GEMM_TOL_F32, "fused tile M=16")
+    ac, asc, aal = nv.nvfp4_quantize(x)
+    assert torch.equal(y, nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.float32))
+    parity.assert_gemm_close(host(y), ref, parity.GEMM_TOL_F32, "quantize into workspace M=16")
+    small = torch.empty(max(nv.quantize_workspace_size(M, K), 16), dtype=torch.uint8, device="cuda")
+    y2, alpha2 = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=torch.float32, workspace=small)
+    assert host(alpha2)[0] == A[2]
+    parity.assert_gemm_close(host(y2), ref, parity.GEMM_TOL_F32, "fused tile M=16")
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 300, 4128), (32, 4096, 4096), (33, 520, 12288), (64, 6144, 4096),
+                                   (64, 4096, 12288), (48, 6200, 12320), (64, 24576, 512)])
+def test_decode_split_k_vs_unsplit(nv, oracle_mod, M, N, K):
+    """Batches above 16 split K over workgroups when given the workspace
+    (partial tiles summed in slice order by a second kernel); without it the
+    same kernels run unsplit.  NVFP4 and BF16: both ways within the gate of
+    the exact product, BF16 output equal to the rounded FP32 output, and
+    nvfp4_quant_gemm equal to quantize + gemm bit for bit."""
+    import torch
+
+    g = np.random.default_rng(M * 3 + N + K)
+    a = wl.activations(M, K, g)
+    wt = wl.weights(N, K, g)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    wc, wsc, wal = u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]])
+    x = bf16_dev(a)
+    ac, asc, aal = nv.nvfp4_quantize(x)
+    ref = oracle_mod.gemm_exact(*A, *W)
+    ref_bf = oracle_mod.bf16_gemm(a, wt)
+    say("decode split-K", M, N, K, "nvfp4 ws", nv.gemm_workspace_size(M, N, K),
+        "bf16 ws", nv.bf16_gemm_workspace_size(M, N, K))
+    for ws in (None, False):
+        y32 = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.float32, workspace=ws)
+        y16 = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=torch.bfloat16, workspace=ws)
+        parity.assert_gemm_close(host(y32), ref, parity.GEMM_TOL_F32, f"nvfp4 {M}x{N}x{K} ws={ws}")
+        assert np.array_equal(bf16_out_to_f64(y16), _bf16_rne(host(y32))), "BF16 output is not the rounded FP32"
+        if ws is None:
+            yq, _ = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=torch.float32)
+            assert torch.equal(yq, y32), "nvfp4_quant_gemm differs from quantize + gemm"
+        b32 = nv.bf16_gemm(x, bf16_dev(wt), out_dtype=torch.float32, workspace=ws)
+        b16 = nv.bf16_gemm(x, bf16_dev(wt), out_dtype=torch.bfloat16, workspace=ws)
+        parity.assert_gemm_close(host(b32), ref_bf, parity.GEMM_TOL_F32, f"bf16 {M}x{N}x{K} ws={ws}")
+        assert np.array_equal(bf16_out_to_f64(b16), _bf16_rne(host(b32))), "BF16 output is not the rounded FP32"

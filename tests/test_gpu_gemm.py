@@ -188,27 +188,50 @@ def test_qwen3_8b_m8192_sampled(nv, oracle_mod, layer):
     assert np.array_equal(got, _bf16_rne(got32)), f"{name}: BF16 output is not the rounded FP32 output"
 
 
-def test_fused_equals_unfused_and_oracle(nv, oracle_mod):
+def _small_workspace(nv, M, K):
+    """A workspace that holds only the dynamic alpha's partials: nvfp4_quant_gemm
+    then quantizes inside the tile kernel's operand staging."""
     import torch
 
-    for (M, N, K) in ((128, 256, 256), (200, 136, 528), (1024, 512, 4096)):
-        g = np.random.default_rng(M + N + K)
-        a = wl.to_bf16_bits(g.standard_t(4.0, size=(M, K)).astype(np.float32))
-        wt = wl.to_bf16_bits(g.standard_normal((N, K), dtype=np.float32) * 0.02)
-        A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
-        wc, wsc, wal = _dev_operand(W)
-        x = bf16_dev(a)
-        for od in (torch.float32, torch.bfloat16):
-            say("fused vs unfused", M, N, K, od)
-            ac, asc, aal = nv.nvfp4_quantize(x)
-            y_unf = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=od)
-            y_fus, alpha = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=od)
+    return torch.empty(max(nv.quantize_workspace_size(M, K), 16), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 256), (200, 136, 528), (1024, 512, 4096),
+                                   # edge tiles, K tail, and the 256 x 256 tile with edges
+                                   (300, 520, 784), (4000, 4100, 4112)])
+def test_fused_equals_unfused_and_oracle(nv, oracle_mod, M, N, K):
+    """nvfp4_quant_gemm, both ways: with its full workspace (quantize into the
+    workspace, then the NVFP4 GEMM) and with only the amax partials (the tile
+    kernel quantizes in its operand staging): alpha and outputs equal
+    nvfp4_quantize followed by nvfp4_gemm bit for bit, dynamic and static."""
+    import torch
+
+    g = np.random.default_rng(M + N + K)
+    a = wl.to_bf16_bits(g.standard_t(4.0, size=(M, K)).astype(np.float32))
+    wt = wl.to_bf16_bits(g.standard_normal((N, K), dtype=np.float32) * 0.02)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    wc, wsc, wal = _dev_operand(W)
+    x = bf16_dev(a)
+    for od in (torch.float32, torch.bfloat16):
+        ac, asc, aal = nv.nvfp4_quantize(x)
+        y_unf = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=od)
+        for full in (True, False):
+            say("fused vs unfused", M, N, K, od, "full workspace" if full else "prologue")
+            ws = None if full else _small_workspace(nv, M, K)
+            y_fus, alpha = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=od, workspace=ws)
             assert host(alpha)[0] == host(aal)[0] == A[2]
             assert torch.equal(y_unf, y_fus), "fused and unfused paths must agree bit for bit"
-            ys, _ = nv.nvfp4_quant_gemm(x, wc, wsc, wal, a_alpha=f32_dev([A[2]]), static_alpha=True, out_dtype=od)
+            ys, _ = nv.nvfp4_quant_gemm(x, wc, wsc, wal, a_alpha=f32_dev([A[2]]), static_alpha=True, out_dtype=od,
+                                        workspace=ws)
             assert torch.equal(ys, y_fus)
+    if M * N <= 1 << 20:
         ref = oracle_mod.gemm_exact(*A, *W)
         parity.assert_gemm_close(y_fus.float().cpu().numpy(), ref, parity.GEMM_TOL_BF16, f"fused {M}x{N}x{K}")
+    else:
+        mi, ni = _sample_pairs(M, N, 2000, M + N)
+        ref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
+        got = y_fus[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].float().cpu().numpy()
+        parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, f"fused {M}x{N}x{K} sampled")
 
 
 def test_fused_student_t_long_prefill_sampled(nv, oracle_mod):
@@ -222,12 +245,15 @@ def test_fused_student_t_long_prefill_sampled(nv, oracle_mod):
     A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
     say("fused gemm student-t m32768", name, (w.M, N, K))
     wc, wsc, wal = _dev_operand(W)
-    y, alpha = nv.nvfp4_quant_gemm(bf16_dev(a), wc, wsc, wal, out_dtype=torch.bfloat16)
-    assert host(alpha)[0] == A[2]
+    x = bf16_dev(a)
     mi, ni = _sample_pairs(w.M, N, 4096, 99)
     ref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
-    got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].float().cpu().numpy()
-    parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, "fused student-t sampled")
+    for full in (True, False):
+        y, alpha = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=torch.bfloat16,
+                                       workspace=None if full else _small_workspace(nv, w.M, K))
+        assert host(alpha)[0] == A[2]
+        got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].float().cpu().numpy()
+        parity.assert_gemm_close(got, ref, parity.GEMM_TOL_BF16, f"fused student-t sampled (full ws {full})")
 
 
 # ------------------------------------------------------------------ BF16 path
