@@ -37,6 +37,7 @@ F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 MFMA
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 ROT = 3                     # rotated input sets of the prefill step
 METRIC = "NVFP4 prefill GEMM TFLOPS (incl. act quant), % FP4 MFMA peak, speedup vs BF16"
+EXTRAS = ("bf16", "sweep", "fused", "quant_out", "mxfp4", "decode")
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_gemm_qwen3_8b_m8192_gate_up_counters.md")
 
 
@@ -47,6 +48,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--no-extras", action="store_true", help="only the headline NVFP4 prefill timing")
+    p.add_argument("--extras", default=",".join(EXTRAS),
+                   help="comma-separated subset of the timings beside the headline: " + ", ".join(EXTRAS))
     p.add_argument("--workload", default="qwen3_8b_m8192",
                    choices=["qwen3_8b_m8192", "qwen3_8b_m32768_t4", "qwen3_32b_m16384"],
                    help="prefill linears to time (default: Qwen3-8B at 8192 tokens, the headline)")
@@ -251,8 +254,12 @@ def main():
     }
 
     print(f"bench: headline {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    if not args.no_extras:
-        result.update(extras(args, nv, wl, layers, sets, M, flops_step, step_ms, sweep=headline))
+    parts = set() if args.no_extras else {x.strip() for x in args.extras.split(",") if x.strip()}
+    if parts - set(EXTRAS):
+        print(f"bench.py: unknown --extras {sorted(parts - set(EXTRAS))}", file=sys.stderr)
+        return 2
+    if parts:
+        result.update(extras(args, nv, wl, layers, sets, M, flops_step, step_ms, parts, sweep=headline))
         print("bench: extras done", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
@@ -261,12 +268,33 @@ def main():
     return 0
 
 
-def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False):
+def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, parts, sweep=False):
     import torch
 
     dev = torch.device("cuda", 0)
     out = {}
     reps = max(3, min(args.steps, 20) // 2)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bf16_ms = None
+    if "bf16" in parts:
+        bf16_ms = _bf16_prefill(nv, sets, reps, s, e)
+        out["bf16_tflops"] = round(flops_step / (bf16_ms * 1e-3) / 1e12, 2)
+        out["speedup_vs_bf16"] = round(bf16_ms / nvfp4_step_ms, 3)
+    if sweep and "sweep" in parts:
+        out["prefill_sweep"] = _phase_split_sweep(nv, wl, layers, sets, M, reps, s, e, nvfp4_step_ms, bf16_ms)
+    if "fused" in parts:
+        out.update(_fused(nv, layers, sets, M, flops_step, reps, s, e))
+    if "quant_out" in parts:
+        out.update(_quant_out(nv, layers, M, flops_step, reps, s, e))
+    if "mxfp4" in parts:
+        out.update(_mxfp4(nv, wl, layers, M, flops_step, reps, s, e, bf16_ms))
+    if "decode" in parts:
+        out.update(_decode(nv, wl, layers, s, e))
+    return out
+
+
+def _bf16_prefill(nv, sets, reps, s, e):
+    import torch
 
     # BF16 prefill GEMMs at the same shapes (the speedup denominator), on the
     # same rotated input sets as the NVFP4 steps
@@ -275,68 +303,76 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
             nv.bf16_gemm(L["x"], L["w_bf16"], out=L["y"])
     for i in range(ROT):
         bf16_step(i)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record()
     for i in range(reps):
         bf16_step(i)
     e.record()
     torch.cuda.synchronize()
-    bf16_ms = s.elapsed_time(e) / reps
-    out["bf16_tflops"] = round(flops_step / (bf16_ms * 1e-3) / 1e12, 2)
-    out["speedup_vs_bf16"] = round(bf16_ms / nvfp4_step_ms, 3)
+    return s.elapsed_time(e) / reps
 
-    # Phase-split sweep: NVFP4 prefill (dynamic-alpha quantizer + GEMM, BF16
-    # out) against the BF16 GEMM at other token counts, same weights; the
-    # activations are the first rows of the headline ones, or those rows
-    # repeated
-    if sweep:
-        def timed_ms(step):
-            for i in range(ROT):
-                step(i)
-            torch.cuda.synchronize()
-            s.record()
-            for i in range(reps):
-                step(i)
-            e.record()
-            torch.cuda.synchronize()
-            return s.elapsed_time(e) / reps
 
-        sw = {}
-        for Ms in wl.PHASE_SPLIT_PREFILL_M:
-            fl = sum(wl.flops(Ms, L["N"], L["K"]) for L in layers)
-            if Ms == M:
-                t4, t16 = nvfp4_step_ms, bf16_ms
-            else:
-                if Ms > M and Ms % M:
-                    continue
-                bufs = []
-                for L in layers:
-                    x = (L["x"][:Ms] if Ms <= M else L["x"].repeat(Ms // M, 1)).contiguous()
-                    bufs.append(dict(x=x, ac=torch.empty((Ms, L["K"] // 2), dtype=torch.uint8, device=dev),
-                                     asc=torch.empty((Ms, L["K"] // 16), dtype=torch.uint8, device=dev),
-                                     aal=torch.empty(1, dtype=torch.float32, device=dev),
-                                     wsb=torch.empty(max(nv.quantize_workspace_size(Ms, L["K"]), 4),
-                                                     dtype=torch.uint8, device=dev),
-                                     y=torch.empty((Ms, L["N"]), dtype=torch.bfloat16, device=dev)))
+def _phase_split_sweep(nv, wl, layers, sets, M, reps, s, e, nvfp4_step_ms, bf16_ms):
+    """NVFP4 prefill (dynamic-alpha quantizer + GEMM, BF16 out) against the
+    BF16 GEMM at other token counts, same weights; the activations are the
+    first rows of the headline ones, or those rows repeated."""
+    import torch
 
-                # the weights rotate over the same copies as in the headline
-                # step (three sets: the NVFP4 weights of one set would
-                # otherwise stay in the Infinity Cache from rep to rep)
-                def nv_step(i):
-                    for L, B in zip(sets[i % ROT], bufs):
-                        nv.nvfp4_quantize(B["x"], B["ac"], B["asc"], B["aal"], workspace=B["wsb"])
-                        nv.nvfp4_gemm(B["ac"], B["asc"], B["aal"], L["wc"], L["ws"], L["wa"], out=B["y"],
-                                      workspace=False)
+    dev = torch.device("cuda", 0)
 
-                def bf_step(i):
-                    for L, B in zip(sets[i % ROT], bufs):
-                        nv.bf16_gemm(B["x"], L["w_bf16"], out=B["y"], workspace=False)
-                t4, t16 = timed_ms(nv_step), timed_ms(bf_step)
-                del bufs
-            sw[str(Ms)] = {"nvfp4_tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
-                           "bf16_tflops": round(fl / (t16 * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(t16 / t4, 3)}
-        out["prefill_sweep"] = sw
+    def timed_ms(step):
+        for i in range(ROT):
+            step(i)
+        torch.cuda.synchronize()
+        s.record()
+        for i in range(reps):
+            step(i)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    sw = {}
+    for Ms in wl.PHASE_SPLIT_PREFILL_M:
+        fl = sum(wl.flops(Ms, L["N"], L["K"]) for L in layers)
+        if Ms == M and bf16_ms is not None:
+            t4, t16 = nvfp4_step_ms, bf16_ms
+        else:
+            if Ms > M and Ms % M:
+                continue
+            bufs = []
+            for L in layers:
+                x = (L["x"][:Ms] if Ms <= M else L["x"].repeat(Ms // M, 1)).contiguous()
+                bufs.append(dict(x=x, ac=torch.empty((Ms, L["K"] // 2), dtype=torch.uint8, device=dev),
+                                 asc=torch.empty((Ms, L["K"] // 16), dtype=torch.uint8, device=dev),
+                                 aal=torch.empty(1, dtype=torch.float32, device=dev),
+                                 wsb=torch.empty(max(nv.quantize_workspace_size(Ms, L["K"]), 4),
+                                                 dtype=torch.uint8, device=dev),
+                                 y=torch.empty((Ms, L["N"]), dtype=torch.bfloat16, device=dev)))
+
+            # the weights rotate over the same copies as in the headline
+            # step (three sets: the NVFP4 weights of one set would
+            # otherwise stay in the Infinity Cache from rep to rep)
+            def nv_step(i):
+                for L, B in zip(sets[i % ROT], bufs):
+                    nv.nvfp4_quantize(B["x"], B["ac"], B["asc"], B["aal"], workspace=B["wsb"])
+                    nv.nvfp4_gemm(B["ac"], B["asc"], B["aal"], L["wc"], L["ws"], L["wa"], out=B["y"],
+                                  workspace=False)
+
+            def bf_step(i):
+                for L, B in zip(sets[i % ROT], bufs):
+                    nv.bf16_gemm(B["x"], L["w_bf16"], out=B["y"], workspace=False)
+            t4, t16 = timed_ms(nv_step), timed_ms(bf_step)
+            del bufs
+        sw[str(Ms)] = {"nvfp4_tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
+                       "bf16_tflops": round(fl / (t16 * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(t16 / t4, 3)}
+    return sw
+
+
+def _fused(nv, layers, sets, M, flops_step, reps, s, e):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    out = {}
 
     # nvfp4_quant_gemm (BF16 activations in, dynamic alpha), on the same
     # rotated sets: with its full workspace it quantizes once into the
@@ -364,9 +400,16 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
     out["fused_tflops"] = round(flops_step / (fused_ms_of(True) * 1e-3) / 1e12, 2)
     out["fused_prologue_tflops"] = round(flops_step / (fused_ms_of(False) * 1e-3) / 1e12, 2)
     del qg_ws
+    return out
 
-    # NVFP4 GEMM whose epilogue quantizes Y to NVFP4 for the next layer
-    # (static output scale), same layers and activations
+
+def _quant_out(nv, layers, M, flops_step, reps, s, e):
+    """NVFP4 GEMM whose epilogue quantizes Y to NVFP4 for the next layer
+    (static output scale), same layers and activations."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    out = {}
     yq = [(torch.empty((M, L["N"] // 2), dtype=torch.uint8, device=dev),
            torch.empty((M, L["N"] // 16), dtype=torch.uint8, device=dev)) for L in layers]
     y_alpha = torch.tensor([0.02], dtype=torch.float32, device=dev)
@@ -384,9 +427,16 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
     torch.cuda.synchronize()
     out["quant_out_gemm_tflops"] = round(flops_step / (s.elapsed_time(e) / reps * 1e-3) / 1e12, 2)
     del yq
+    return out
 
-    # MXFP4 (E2M1 + E8M0 per 32) prefill of the same layers on the block-scaled
-    # FP4 MFMA: activation quantizer + GEMM, weights quantized once
+
+def _mxfp4(nv, wl, layers, M, flops_step, reps, s, e, bf16_ms):
+    """MXFP4 (E2M1 + E8M0 per 32) prefill of the same layers on the
+    block-scaled FP4 MFMA: activation quantizer + GEMM, weights quantized once."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    out = {}
     mx = []
     for L in layers:
         wc, ws = nv.mxfp4_quantize(L["w_bf16"])
@@ -414,10 +464,18 @@ def extras(args, nv, wl, layers, sets, M, flops_step, nvfp4_step_ms, sweep=False
     mx_ms = s.elapsed_time(e) / reps
     out["mxfp4_prefill_tflops"] = round(flops_step / (mx_ms * 1e-3) / 1e12, 2)
     out["mxfp4_frac_fp4_peak"] = round(flops_step / (mx_ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4)
-    out["mxfp4_speedup_vs_bf16"] = round(bf16_ms / mx_ms, 3)
+    if bf16_ms is not None:
+        out["mxfp4_speedup_vs_bf16"] = round(bf16_ms / mx_ms, 3)
     out["mxfp4_gemm_tflops"] = {L["name"]: round(wl.flops(M, L["N"], L["K"]) / (mt.total_ms(("mxgemm", L["name"])) / reps
                                                                               * 1e-3) / 1e12, 1) for L in layers}
+    return out
 
+
+def _decode(nv, wl, layers, s, e):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    out = {}
     # Decode steps (one token batch through the four layers) are replayed from
     # HIP graphs, as a serving loop runs them: per-call host overhead would
     # otherwise exceed these kernels' GPU time.  Weights rotate over copies

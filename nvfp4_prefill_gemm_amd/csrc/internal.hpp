@@ -32,7 +32,7 @@ hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, i
 // Small tensors (rows * cols <= kSelfAmaxMaxElems, e.g. decode batches) take
 // a single launch in dynamic mode: every workgroup of the quantize pass reads
 // the whole tensor for its amax, and no amax pass (nor its partials) is used.
-constexpr int64_t kSelfAmaxMaxElems = int64_t(1) << 17;
+constexpr int64_t kSelfAmaxMaxElems = int64_t(1) << 15;
 bool quantize_self_amax(int64_t rows, int64_t cols);
 
 // dynamic != 0: alpha = amax / 2688 is written to *alpha, the amax taken from

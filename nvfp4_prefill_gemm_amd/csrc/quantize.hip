@@ -116,31 +116,32 @@ __global__ __launch_bounds__(kThreads) void alpha_kernel(const uint32_t *__restr
 // amax pass's partials, or the workgroup's own pass over a small tensor.
 enum AlphaSrc { ALPHA_STATIC = 0, ALPHA_PARTIALS = 1, ALPHA_SELF = 2 };
 
-// Max |x| over a whole small tensor by one workgroup (FP32 bits of the BF16
-// maximum): every workgroup of the single-launch mode reads the tensor once
-// from L2 instead of waiting for a separate amax launch.
+// Max |x| over a whole small tensor (at most kSelfLoads * kThreads octets)
+// by one workgroup, as FP32 bits of the BF16 maximum: every workgroup of the
+// single-launch mode reads the tensor once, all its loads in flight together,
+// instead of waiting for a separate amax launch.
+constexpr int kSelfLoads = 16;
 __device__ __forceinline__ uint32_t tensor_amax_bits(const uint16_t *__restrict__ x, uint32_t rows, uint32_t octs,
                                                      int64_t ld) {
-    ushort2_t m = {0, 0};
     const uint32_t total = rows * octs;
-    for (uint32_t o0 = threadIdx.x; o0 < total; o0 += kThreads * 4) {
-        uint4 v[4];
+    uint4 v[kSelfLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t o = o0 + u * kThreads, r = o < total ? o / octs : 0u;
-            v[u] = o < total ? *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (o - r * octs) * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
+    for (int u = 0; u < kSelfLoads; ++u) {
+        const uint32_t o = threadIdx.x + u * kThreads, r = o < total ? o / octs : 0u;
+        v[u] = o < total ? *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (o - r * octs) * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    ushort2_t m = {0, 0};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
-            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
-            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
-            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
-        }
+    for (int u = 0; u < kSelfLoads; ++u) {
+        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
+        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
+        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
+        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
     }
     return max((uint32_t)m.x, (uint32_t)m.y) << 16;
 }
+static_assert(kSelfLoads * kThreads * 8 >= kSelfAmaxMaxElems, "the single-launch amax reads the whole tensor");
 
 template <int kAlpha>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__restrict__ x, int64_t rows,
