@@ -39,6 +39,8 @@ ROT = 3                     # rotated input sets of the prefill step
 METRIC = "NVFP4 prefill GEMM TFLOPS (incl. act quant), % FP4 MFMA peak, speedup vs BF16"
 EXTRAS = ("bf16", "sweep", "fused", "quant_out", "mxfp4", "decode")
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_gemm_qwen3_8b_m8192_gate_up_counters.md")
+# the tile GEMM's sources: a counter summary describes the kernel built from these
+GEMM_SOURCES = ("gemm.hip", "nvfp4_device.hpp", "epilogue.hpp", "tiling.hpp")
 
 
 def parse_args():
@@ -86,7 +88,7 @@ def _traffic_from_profile():
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("gemm_source_sha256_16") != _source_hash("gemm.hip", "nvfp4_device.hpp"):
+    if vals.get("gemm_source_sha256_16") != _source_hash(*GEMM_SOURCES):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

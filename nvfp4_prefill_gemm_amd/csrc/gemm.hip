@@ -35,6 +35,7 @@
 
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
+#include "epilogue.hpp"
 #include "tiling.hpp"
 
 namespace nvfp4 {
@@ -82,6 +83,7 @@ struct GemmArgs {
     uint8_t *out_scales;      // NVFP4 output: E4M3 block scales [M, N/16]
     const float *out_alpha;   // NVFP4 output: static tensor scale
     int rows_rsrc = 0;        // edge tiles may address a tile's rows through one buffer resource (< 2^31 bytes)
+    bool vec = false;         // FP32/BF16 output: out and ld_out allow 16-byte stores
 };
 
 // ---------------------------------------------------------------- loaders
@@ -522,6 +524,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
             // operands: +1.5-2% over the compiler's grouping (same-process A/B
             // on the Qwen3-8B layers at 8192 tokens; two and four VALU
             // operations per MFMA measured slower, four and six the same)
+            // BF16: the same for its staging copies (two or three MFMAs per
+            // LDS write): +5% on the Qwen3-8B layers at 8192 tokens
+            if constexpr (kKind == KIND_BF16) {
+                if (do_store && ks < 3) {
+                    if (ks == 2) {
+                        static_for<4>([&](auto) __attribute__((always_inline)) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                        });
+                    } else {
+                        static_for<2>([&](auto) __attribute__((always_inline)) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                        });
+                    }
+                }
+            }
             if constexpr (kKind == KIND_NVFP4) {
                 if (do_store && ks < 3) {
                     if (ks == 2) {  // both halves of W
@@ -668,24 +687,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
         });
         return;
     } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn * C::WN + j * 32 + (lane & 31);
-            if (kGuard && col >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * C::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (kGuard && row >= g.M) continue;
-                float y = acc[i][j][r];
-                if (kKind != KIND_BF16) y = (y * sa) * sw;
-                if (kOut == OUT_BF16)
-                    reinterpret_cast<__bf16 *>(g.out)[row * g.ld_out + col] = (__bf16)y;
-                else
-                    reinterpret_cast<float *>(g.out)[row * g.ld_out + col] = y;
-            }
-        }
+        // staged through a per-wave LDS slab (the operand buffers are free
+        // once every wave has left the main loop) for 16-byte row stores
+        static_assert(NT / 64 * epilogue_slab_floats<TN>() * 4 <= 2 * (BM + BN) * BK * 2, "slabs fit the LDS");
+        __syncthreads();
+        float *slab = reinterpret_cast<float *>(lds) + wave * epilogue_slab_floats<TN>();
+        store_acc_tiles<TM, TN, kOut == OUT_BF16>(acc, sa, sw, slab, g.out, g.ld_out, m0 + wm * C::WM,
+                                                  n0 + wn * C::WN, g.M, g.N, g.vec);
     }
 }
 
@@ -725,6 +733,7 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     GemmArgs ga = g;
     const int64_t a_row = kKind == KIND_NVFP4 ? g.K / 2 : g.lda * 2, w_row = kKind == KIND_BF16 ? g.K * 2 : g.K / 2;
     ga.rows_rsrc = C::BM * a_row < (int64_t(1) << 31) && C::BN * w_row < (int64_t(1) << 31);
+    ga.vec = kOut != OUT_NVFP4 && epilogue_vec_ok(g.out, g.ld_out, kOut == OUT_F32 ? 4 : 2);
     static std::atomic<uint32_t> attr_done{0};
     if (hipError_t e = set_dyn_lds_once(attr_done, (const void *)kern, (int)lds_bytes); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds_bytes, s, ga);

@@ -20,6 +20,7 @@
 
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
+#include "epilogue.hpp"
 #include "tiling.hpp"
 
 namespace nvfp4 {
@@ -98,6 +99,7 @@ struct MxArgs {
     int64_t M, N, K;
     void *out;
     int64_t ld_out;
+    bool vec;  // out and ld_out allow 16-byte stores
 };
 
 __device__ __forceinline__ int code_off(int row, int chunk) { return row * MKB + ((chunk ^ lds_swz(row)) << 4); }
@@ -131,26 +133,18 @@ struct MxRegs {
     u32x4_t a0, a1, w0, w1;
 };
 
+// Epilogue: every wave stages its 128 x 64 result through LDS (after a
+// barrier: the operand stages are free) and writes 16-byte row pieces.
 template <bool kOutBf16>
-__device__ __forceinline__ void mx_store(const MxArgs &g, const f32x16_t (&acc)[MTM][MTN], int64_t m0, int64_t n0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void mx_store(const MxArgs &g, const f32x16_t (&acc)[MTM][MTN], int64_t m0, int64_t n0,
+                                         uint8_t *smem) {
+    static_assert(MNT / 64 * epilogue_slab_floats<MTN>() * 4 <= 2 * STAGE, "epilogue slabs fit the kernel's LDS");
+    const int wave = threadIdx.x >> 6;
     const int wm = wave / MWGN, wn = wave % MWGN;
-#pragma unroll
-    for (int i = 0; i < MTM; ++i)
-#pragma unroll
-        for (int j = 0; j < MTN; ++j) {
-            const int64_t col = n0 + wn * MWN + j * 32 + (lane & 31);
-            if (col >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * MWM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row >= g.M) continue;
-                if (kOutBf16)
-                    reinterpret_cast<__bf16 *>(g.out)[row * g.ld_out + col] = (__bf16)acc[i][j][r];
-                else
-                    reinterpret_cast<float *>(g.out)[row * g.ld_out + col] = acc[i][j][r];
-            }
-        }
+    __syncthreads();
+    float *slab = reinterpret_cast<float *>(smem) + wave * epilogue_slab_floats<MTN>();
+    store_acc_tiles<MTM, MTN, kOutBf16>(acc, 1.0f, 1.0f, slab, g.out, g.ld_out, m0 + wm * MWM, n0 + wn * MWN, g.M,
+                                        g.N, g.vec);
 }
 
 // k64 sub-step ks of a step: 4 x 2 scaled MFMAs; the lane's scale is byte 2 ks
@@ -313,7 +307,7 @@ __device__ __forceinline__ void mx_tile_pipe(const MxArgs &g, uint8_t *smem, int
         step(kt + 2, std::integral_constant<int, 2>());
         step(kt + 3, std::integral_constant<int, 3>());
     }
-    mx_store<kOutBf16>(g, acc, m0, n0);
+    mx_store<kOutBf16>(g, acc, m0, n0, smem);
 }
 
 // Edge tiles and K % 512 != 0: K step 256, two LDS stages staged through
@@ -415,7 +409,7 @@ __device__ __forceinline__ void mx_tile_staged(const MxArgs &g, uint8_t *smem, i
         }
         __syncthreads();
     }
-    mx_store<kOutBf16>(g, acc, m0, n0);
+    mx_store<kOutBf16>(g, acc, m0, n0, smem);
 }
 
 template <bool kOutBf16>
@@ -460,7 +454,8 @@ hipError_t launch_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int
 hipError_t launch_mx_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
                           const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *out, int out_type,
                           int64_t ld_out, hipStream_t s) {
-    MxArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K, out, ld_out};
+    MxArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K, out, ld_out,
+             epilogue_vec_ok(out, ld_out, out_type == OUT_BF16 ? 2 : 4)};
     return out_type == OUT_BF16 ? launch_mx<true>(g, s) : launch_mx<false>(g, s);
 }
 

@@ -21,7 +21,7 @@ def test_traffic_only_for_the_profiled_source(monkeypatch, tmp_path):
     import bench
 
     prof = tmp_path / "counters.md"
-    cur = bench._source_hash("gemm.hip", "nvfp4_device.hpp")
+    cur = bench._source_hash(*bench.GEMM_SOURCES)
     prof.write_text(f"- gemm_source_sha256_16: `{cur}`\n- hbm_bytes_per_launch: `1.25e+09`\n")
     monkeypatch.setattr(bench, "PROFILE_COUNTERS", str(prof))
     assert bench._traffic_from_profile() == 1.25e9

@@ -92,9 +92,9 @@ def test_quant_out_qwen3_8b_o_proj_full(nv, oracle_mod):
     name, K, N = w.linears[1]
     a, wt = wl.layer_inputs(w, 1)
     say("gemm quant out qwen3-8b", name, (w.M, N, K))
-    ac, asc, aal = nv.nvfp4_quantize(bf16_dev(a))
-    A = (host(ac), host(asc), host(aal)[0])
-    W = oracle_mod.quantize(wt)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    ac, asc, aal = nv.nvfp4_quantize(bf16_dev(a))  # the library's quantizer on the way in: bit-exact
+    assert host(aal)[0] == A[2] and np.array_equal(host(asc), A[1]) and np.array_equal(host(ac), A[0])
     y_alpha = np.float32(0.02)
     g = np.random.default_rng(5)
     mi = np.concatenate([g.integers(0, w.M, 4096), [0, w.M - 1]])
