@@ -78,6 +78,9 @@ struct DecodePlan {
     int ng, waves, u, s;  // 16-column groups per workgroup, waves, K steps per stage, K slices
 };
 DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K);
+// NVFP4 decode of one or two batch rows with K % 128 == 0 runs the weight
+// codes through the FP4 MFMA (block partial sums scaled afterwards).
+inline bool decode_fp4_form(int64_t M, int64_t K) { return M <= 2 && (K & 127) == 0; }
 // Workspace bytes of the plan's split-K partials (0 without a split).
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K);
 

@@ -28,7 +28,10 @@
 // holds K = 128c + 32g + 8t + i on both operands (the same permutation of K
 // for A and W, which leaves the dot product unchanged).  Codes are expanded
 // exactly to q * sigma in FP16 in registers; alpha_A * alpha_W is applied in
-// the epilogue as in the prefill GEMM.
+// the epilogue as in the prefill GEMM.  Batches of one or two rows with
+// K % 128 == 0 skip the expansion: the same 16-byte code loads feed the FP4
+// MFMA, whose spare rows separate the 16-element blocks, and each block's
+// exact partial sum is scaled by sigma_A * sigma_W in FP32 (see kF4 below).
 //
 // Fused decode (nvfp4_quant_gemm with M * K <= 196608): the workgroup first
 // quantizes the part of the BF16 batch its K slice needs, one 8-element group
@@ -49,6 +52,11 @@ namespace nvfp4 {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 
 // Epilogue of a decode workgroup: the final output (FP32 or BF16, y =
 // (sum * sa) * sw), or the raw FP32 partial of K slice blockIdx.y into the
@@ -179,13 +187,26 @@ enum ASrc { A_NVFP4 = 0, A_BF16_DYNAMIC = 1, A_BF16_STATIC = 2 };
 // 16-byte aligned codes and 4-byte aligned scales.  kA != A_NVFP4: A is
 // BF16 [M, ld_x] (16-byte aligned rows, MG == 1), quantized into LDS
 // (M * K * 9 / 16 bytes of dynamic shared memory; the slice's part is filled).
-template <int MG, int NG, int WAVES, int U, int kOut, int kA = A_NVFP4>
+//
+// kF4 (M <= 2, K % 128 == 0, MG == 1): the weight codes go to the FP4 MFMA
+// as they are loaded.  One v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0
+// scales) per 128-wide chunk and 16 weight rows: A row r holds block r % 8 of
+// the chunk for batch row r / 8 and zeros elsewhere, so output element
+// (r, n) is that block's partial sum of E2M1 products, exact in FP32 (at most
+// 16 products of magnitude <= 36, multiples of 1/4).  It is then scaled by
+// sigma_A * sigma_W (exact: two 4-bit significands) and added to the lane's
+// FP32 accumulator for that block position, so no code is expanded to FP16.
+// A lane holds rows 4 (l / 16) + i, i.e. batch row l / 32 and blocks
+// 4 ((l / 16) % 2) + i of every chunk; the four block sums of a lane and the
+// two lanes of a batch row are added at the end.
+template <int MG, int NG, int WAVES, int U, int kOut, int kA = A_NVFP4, bool kF4 = false>
 __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, float *__restrict__ a_alpha,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, const float *__restrict__ w_alpha, int64_t M,
     int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out, const uint16_t *__restrict__ x, int64_t ld_x,
     int64_t sps) {
     static_assert(kA == A_NVFP4 || MG == 1, "BF16 activations: one 16-row group");
+    static_assert(!kF4 || MG == 1, "the FP4-MFMA path takes at most two batch rows");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int64_t cb = K >> 1, sb = K >> 4;  // code and scale bytes per row
@@ -221,12 +242,26 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         xco[i] = (uint32_t)((xv[i] ? m : 0) * cb);
         xso[i] = (uint32_t)((xv[i] ? m : 0) * sb);
     }
+    // kF4: this lane's A-operand piece (8 code bytes of block fr % 8 of batch
+    // row fr / 8, in half fr % 2 of the lane's 32 K, when that block lies in
+    // the lane's K range) and its output rows' scale words (4 bytes: blocks
+    // 4 (fg % 2) .. + 3 of the chunk, for batch row lane / 32 and weight row n)
+    const int fr = lane & 15, fg = lane >> 4;
+    const bool f_act = ((fr & 7) >> 1) == fg && (fr >> 3) < M, f_hi = fr & 1;
+    const bool f_sact = (lane >> 5) < M;
+    const uint32_t f_xo = f_act ? (uint32_t)((fr >> 3) * cb + 8 * (fr & 7)) : 0u;   // + 64 per chunk
+    const uint32_t f_so = (uint32_t)((f_sact ? (lane >> 5) : 0) * sb + 4 * (fg & 1));  // + 8 per chunk
+    uint32_t f_wso[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) f_wso[j] = (uint32_t)((j * 16 + (lane & 15)) * sb + 4 * (fg & 1));
     const uint8_t *lc = nullptr, *ls = nullptr;  // LDS copy of A (fused path)
     float alpha_a = 0.0f;
     // Two register stages of U chunks each, as in the BF16 decode kernel.
     struct NStage {
         uint4 wq[U][NG], xq[U][MG];
         uint32_t wsc[U][NG], xsc[U][MG];
+        uint2 fx[U];  // kF4
+        uint32_t fxs[U], fws[U][NG];
     };
     // weights (w) and the batch (x) of a stage; the fused path issues the
     // first stage's weight loads before it quantizes the batch
@@ -236,6 +271,27 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             const int64_t c = c0 + (int64_t)u * WAVES, k = c * 128 + kg;
             const bool kin = c < ce && k < K;  // K % 32 == 0: the lane's 32 codes are all in or all out
             const uint32_t kc = (uint32_t)(k >> 1), ksc = (uint32_t)(k >> 4);
+            if constexpr (kF4) {  // K % 128 == 0: the whole chunk is in range
+                if (do_w) {
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) {
+                        st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + kc : kBufOOB);
+                        st.fws[u][j] = buf_load4(wss, kin ? f_wso[j] + (uint32_t)c * 8u : kBufOOB);
+                    }
+                }
+                if (!do_x) continue;
+                if constexpr (kA == A_NVFP4) {
+                    st.fx[u] = buf_load8(xcs, (kin & f_act) ? f_xo + (uint32_t)c * 64u : kBufOOB);
+                    st.fxs[u] = buf_load4(xss, (kin & f_sact) ? f_so + (uint32_t)c * 8u : kBufOOB);
+                } else {  // LDS: clamp the address, zero by select
+                    const uint32_t cc = kin ? (uint32_t)c : 0u;
+                    const uint2 q = *reinterpret_cast<const uint2 *>(lc + f_xo + cc * 64u);
+                    const uint32_t sc = *reinterpret_cast<const uint32_t *>(ls + f_so + cc * 8u);
+                    st.fx[u] = (kin & f_act) ? q : make_uint2(0, 0);
+                    st.fxs[u] = (kin & f_sact) ? sc : 0u;
+                }
+                continue;
+            }
             if (do_w) {
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
@@ -261,6 +317,35 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     };
     auto load = [&](int64_t c0, NStage &st) __attribute__((always_inline)) { load_part(c0, st, true, true); };
     auto compute = [&](const NStage &st) __attribute__((always_inline)) {
+        if constexpr (kF4) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint2 xv = st.fx[u];
+                const i32x8_t a8 = {f_hi ? 0 : (int)xv.x, f_hi ? 0 : (int)xv.y, f_hi ? (int)xv.x : 0,
+                                    f_hi ? (int)xv.y : 0, 0, 0, 0, 0};
+                float sa4[4];
+                sa4[0] = __builtin_amdgcn_cvt_f32_fp8((int)st.fxs[u], 0);
+                sa4[1] = __builtin_amdgcn_cvt_f32_fp8((int)st.fxs[u], 1);
+                sa4[2] = __builtin_amdgcn_cvt_f32_fp8((int)st.fxs[u], 2);
+                sa4[3] = __builtin_amdgcn_cvt_f32_fp8((int)st.fxs[u], 3);
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    const uint4 q = st.wq[u][j];
+                    const i32x8_t b8 = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                    const f4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f4_t{0.f, 0.f, 0.f, 0.f},
+                                                                                   4, 4, 0, 127, 0, 127);
+                    const float sw0 = __builtin_amdgcn_cvt_f32_fp8((int)st.fws[u][j], 0);
+                    const float sw1 = __builtin_amdgcn_cvt_f32_fp8((int)st.fws[u][j], 1);
+                    const float sw2 = __builtin_amdgcn_cvt_f32_fp8((int)st.fws[u][j], 2);
+                    const float sw3 = __builtin_amdgcn_cvt_f32_fp8((int)st.fws[u][j], 3);
+                    acc[0][j][0] = __builtin_fmaf(p[0], sa4[0] * sw0, acc[0][j][0]);
+                    acc[0][j][1] = __builtin_fmaf(p[1], sa4[1] * sw1, acc[0][j][1]);
+                    acc[0][j][2] = __builtin_fmaf(p[2], sa4[2] * sw2, acc[0][j][2]);
+                    acc[0][j][3] = __builtin_fmaf(p[3], sa4[3] * sw3, acc[0][j][3]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -405,6 +490,18 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         c0 = c2;
     }
 
+    if constexpr (kF4) {
+        // a lane's four block sums, then the two lanes of its batch row
+        // (blocks 0-3 and 4-7), into the 16x16 layout tile_reduce takes:
+        // lanes 0-15 hold batch rows 0 and 1 of column n = lane
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            float t = ((acc[0][j][0] + acc[0][j][1]) + acc[0][j][2]) + acc[0][j][3];
+            t += __shfl_xor(t, 16);
+            const float t1 = __shfl(t, (lane & 15) + 32);
+            acc[0][j] = lane < 16 ? f4_t{t, t1, 0.f, 0.f} : f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     float sa = 1.0f, sw = 1.0f;
     if constexpr (kOut != DOUT_PARTIAL) {
         sa = kA == A_NVFP4 ? *a_alpha : alpha_a;
@@ -477,8 +574,9 @@ hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int6
     return hipGetLastError();
 }
 
-// NVFP4 decode kernel (kA: NVFP4 activations, or BF16 ones quantized inside).
-template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4>
+// NVFP4 decode kernel (kA: NVFP4 activations, or BF16 ones quantized inside;
+// kF4: the FP4-MFMA form, for M <= 2 and K % 128 == 0).
+template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4, bool kF4 = false>
 hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
                             const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
                             int S, float *part, hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0) {
@@ -488,9 +586,9 @@ hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, con
     const int ns = S > 1 ? (int)((chunks + sps - 1) / sps) : 1;
     const size_t lds = kA == A_NVFP4 ? 0 : (size_t)(M * K / 2 + M * K / 16);
     const int kind = ns > 1 ? DOUT_PARTIAL : out_type == OUT_BF16 ? DOUT_BF16 : DOUT_F32;
-    const void *f = kind == DOUT_PARTIAL ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA>
-                    : kind == DOUT_BF16  ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA>
-                                         : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA>;
+    const void *f = kind == DOUT_PARTIAL ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4>
+                    : kind == DOUT_BF16  ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4>
+                                         : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4>;
     if (kA != A_NVFP4) {
         static std::atomic<uint32_t> attr_done[3];
         if (hipError_t e = set_dyn_lds_once(attr_done[kind], f, (int)(kFusedDecodeMaxElems * 9 / 16)); e != hipSuccess)
@@ -500,13 +598,13 @@ hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, con
     void *dst = ns > 1 ? (void *)part : out;
     const int64_t ld = ns > 1 ? N : ld_out;
     if (kind == DOUT_PARTIAL)
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA>), grid, block, lds, s, ac, as, aa,
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4>), grid, block, lds, s, ac, as, aa,
                            wc, ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     else if (kind == DOUT_BF16)
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA>), grid, block, lds, s, ac, as, aa, wc,
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4>), grid, block, lds, s, ac, as, aa, wc,
                            ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     else
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA>), grid, block, lds, s, ac, as, aa, wc,
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4>), grid, block, lds, s, ac, as, aa, wc,
                            ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if (ns > 1) return launch_reduce(part, ns, M, N, aa, wa, out, out_type, ld_out, s);
@@ -527,6 +625,14 @@ __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, 
 // K so that narrow layers still give about 256 workgroups of wide strips
 // (BF16), or, for NVFP4 whose weights are 3.6x smaller, only on long K.
 DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
+    // the FP4-MFMA form of the NVFP4 kernel (M <= 2, K % 128 == 0), from its
+    // own sweep (fused and unfused, batch 1 and 2): narrower strips and fewer
+    // waves than the FP16-expansion form, two chunks per register stage
+    if (kind != DECODE_BF16 && decode_fp4_form(M, K)) {
+        if (N >= 16384) return {1, 4, 2, 1};
+        if (K >= 8192) return {1, 16, 1, 1};
+        return {1, 8, 2, 1};
+    }
     if (kind == DECODE_BF16) {
         if (M <= 4) return {1, 16, 1, 1};
         if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1};
@@ -564,11 +670,29 @@ hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64
     return launch_bf16_cfg<MG, 1, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
 }
 
+// The FP4-MFMA form (M <= 2, K % 128 == 0) of the plans decode_plan gives it.
+template <int kA>
+hipError_t launch_f4(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
+                     const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
+                     const DecodePlan &p, int S, float *part, hipStream_t s, const uint16_t *x, int64_t ld_x) {
+    if (p.waves == 4)
+        return launch_nvfp4_cfg<1, 1, 4, 2, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                      x, ld_x);
+    if (p.waves == 8)
+        return launch_nvfp4_cfg<1, 1, 8, 2, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                      x, ld_x);
+    return launch_nvfp4_cfg<1, 1, 16, 1, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                   x, ld_x);
+}
+
 template <int MG>
 hipError_t launch_nv_mg(const uint8_t *ac, const uint8_t *as, const float *aa_in, const uint8_t *wc,
                         const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type,
                         int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s) {
     float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
+    if constexpr (MG == 1)
+        if (decode_fp4_form(M, K))
+            return launch_f4<A_NVFP4>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, nullptr, 0);
     if (p.ng == 4) return launch_nvfp4_cfg<MG, 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 2) return launch_nvfp4_cfg<MG, 2, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.waves == 8)
@@ -580,6 +704,9 @@ template <int kA>
 hipError_t launch_fused_a(const uint16_t *x, int64_t ld_x, float *a_alpha, const uint8_t *wc, const uint8_t *ws,
                           const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
                           const DecodePlan &p, int S, float *part, hipStream_t s) {
+    if (decode_fp4_form(M, K))
+        return launch_f4<kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, x,
+                             ld_x);
     if (p.ng == 2)
         return launch_nvfp4_cfg<1, 2, 8, 1, kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, S,
                                                 part, s, x, ld_x);

@@ -87,6 +87,24 @@ def test_decode_nvfp4_ragged(nv, oracle_mod, M, N, K):
     _check(nv, A, W, oracle_mod.gemm_exact(*A, *W), f"decode ragged {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 33, 128), (2, 1000, 256), (1, 6200, 4096), (2, 4096, 12288), (2, 17, 1024),
+                                   (1, 24576, 4096)])
+def test_decode_nvfp4_fp4_mfma_form(nv, oracle_mod, M, N, K):
+    """Batches of one or two rows with K % 128 == 0 run the weight codes
+    through the FP4 MFMA and scale each 16-element block's exact partial sum
+    by sigma_A * sigma_W afterwards: random codes, every E4M3 scale code on
+    both operands (zero, the subnormals, 448), one- and two-group strips."""
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    qa, sa = _random_operand(g, M, K)
+    qw, sw = _random_operand(g, N, K)
+    sa[:] = (np.arange(sa.size, dtype=np.int64).reshape(sa.shape) * 5 % 127).astype(np.uint8)
+    sw[::7, :] = (np.arange(K // 16) % 8).astype(np.uint8)[None, :]  # rows of zero and subnormal scales
+    sw[1::5, ::3] = 0x7E
+    A, W = (qa, sa, np.float32(0.37)), (qw, sw, np.float32(2.0 ** -7))
+    say("decode nvfp4 fp4-mfma form", M, N, K)
+    _check(nv, A, W, oracle_mod.gemm_exact(*A, *W), f"decode fp4 form {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 300, 48), (8, 64, 80), (64, 40, 4112)])
 def test_decode_nvfp4_k_not_multiple_of_32(nv, oracle_mod, M, N, K):
     """K % 32 != 0 takes the tile kernel; results still match the oracle."""
