@@ -12,9 +12,10 @@
 //
 // GEMM: 256 x 256 output tile, 8 waves of 128 x 64 (4 x 2 scaled MFMAs of
 // 32x32x64).  Interior tiles with K % 512 == 0 run a register-staged
-// pipeline with K step 128 and block scales fetched per group of four steps
-// (mx_tile_pipe); edge tiles and other K a simpler loop with K step 256, two
-// LDS stages of 68 KB staged through guarded register loads (mx_tile_staged).
+// pipeline with K step 256 and block scales fetched per group of two steps
+// (mx_tile_pipe256); edge tiles and other K a simpler loop with K step 256,
+// two LDS stages of 68 KB staged through guarded register loads
+// (mx_tile_staged).
 #include <stdlib.h>
 #include <string.h>
 
@@ -104,34 +105,9 @@ struct MxArgs {
 
 __device__ __forceinline__ int code_off(int row, int chunk) { return row * MKB + ((chunk ^ lds_swz(row)) << 4); }
 
-// Pipelined interior tiles (K % 512 == 0): K step 128, two LDS stages of A
-// and W codes (256 rows x 64 bytes each, swizzled 16-byte chunks), and the
-// scales in groups of four steps (16 bytes per row: K 512), two group buffers
-// of 8 KB.  Every fragment read is a register base plus an immediate offset.
-// Operands are staged through registers from buffer loads: step kt + 2 is
-// loaded while step kt computes, and step kt + 1 (loaded one step earlier) is
-// written to LDS between the two k64 sub-steps; the step's one barrier
-// follows, and the next step's fragments and scales are read under the second
-// sub-step's MFMAs.  A row's scales are fetched 16 bytes at a time, once per
-// four steps: fetched per step (4 bytes per row), they made half of the L2
-// requests of the loop for 6% of its bytes.
-constexpr int PKB = 64;                    // code bytes per row per step (128 k)
-constexpr int PCODE = MBM * PKB;           // 16 KB
-constexpr int PW = 2 * PCODE;              // W code stages
-constexpr int PSC = 4 * PCODE;             // scale groups: [2][A 256 x 16 B, W 256 x 16 B]
-constexpr int PSG = 2 * MBM * 16;          // 8 KB per group
+// Interior tiles take the K-256 pipeline below when K % 512 == 0 and a
+// tile's rows span less than 2^31 bytes (32-bit buffer offsets).
 constexpr int64_t kMxPipeMaxK = int64_t(1) << 24;
-static_assert(PSC + 2 * PSG <= 2 * STAGE, "the pipelined stages fit the kernel's LDS");
-
-// 16-byte chunk c (of 4) of row r: slot c ^ ((r / 4) % 4), so the 16 rows a
-// quarter-wave reads at one chunk fall on distinct banks
-__device__ __forceinline__ int pcode_off(int row, int chunk) { return row * PKB + ((chunk ^ ((row >> 2) & 3)) << 4); }
-
-// one step's codes in registers: two 16-byte chunks of A and of W (native
-// vectors: HIP's uint4 wrapper kept these in scratch)
-struct MxRegs {
-    u32x4_t a0, a1, w0, w1;
-};
 
 // Epilogue: every wave stages its 128 x 64 result through LDS (after a
 // barrier: the operand stages are free) and writes 16-byte row pieces.
@@ -167,75 +143,93 @@ __device__ __forceinline__ void mx_mfmas(f32x16_t (&acc)[MTM][MTN], const uint4 
     }
 }
 
+// Pipelined interior tiles, K step 256: a row's 128 code bytes per step
+// are loaded by 8 lanes (each load instruction covers 8 rows x 128 bytes,
+// one 128-byte L2 line per row), one register stage holds step kt + 1 while
+// step kt computes (loaded at the top of the step, written to the other LDS
+// stage before the step's one barrier), four k64 sub-steps, fragments read
+// one sub-step ahead; scales per group of two steps (16 bytes per row:
+// fetched per step, 4 bytes per row, scales had made half of the loop's L2
+// requests for 6% of its bytes).  Against a K-128 step with two register
+// stages and 64-byte row pieces: +2-4% on the Qwen3-8B layers, bit-identical.
+constexpr int QKB = 128;                 // code bytes per row per step
+constexpr int QCODE = MBM * QKB;         // 32 KB
+constexpr int QW = 2 * QCODE;            // W code stages
+constexpr int QSC = 4 * QCODE;           // scale groups: [2][A 256 x 16 B, W 256 x 16 B]
+constexpr int QSG = 2 * MBM * 16;        // 8 KB per group
+constexpr int QLDS = QSC + 2 * QSG;      // 144 KB
+// 16-byte chunk c (of 8) of row r: slot c ^ f(r), f(r) = (r / 2) ^ 4 (r % 2):
+// any 8 aligned rows, and the same-parity rows of any 16 aligned rows, take
+// distinct slots for one chunk
+__device__ __forceinline__ int qcode_off(int row, int chunk) {
+    return row * QKB + ((chunk ^ (((row >> 1) ^ ((row & 1) << 2)) & 7)) << 4);
+}
+
 template <bool kOutBf16>
-__device__ __forceinline__ void mx_tile_pipe(const MxArgs &g, uint8_t *smem, int64_t m0, int64_t n0) {
+__device__ __forceinline__ void mx_tile_pipe256(const MxArgs &g, uint8_t *smem, int64_t m0, int64_t n0) {
     const int lane = threadIdx.x & 63, t = threadIdx.x;
     const int wave = t >> 6;
     const int wm = wave / MWGN, wn = wave % MWGN;
-    const int KT = (int)(g.K / 128);  // a multiple of 4
+    const int KT = (int)(g.K / 256);  // even (K % 512 == 0)
     const uint32_t rb = (uint32_t)(g.K >> 1), sb = (uint32_t)(g.K >> 5);
 
-    // staging: thread t moves chunks t and t + 512 of each code tile (row
-    // i / 4, chunk i % 4) and, once per group, the 16 scale bytes of row t of
-    // A (t < 256) or t - 256 of W; buffer resources over the tile's rows, the
-    // step as the scalar offset
     const rsrc_t ra_ = make_rsrc(g.ac + m0 * (int64_t)rb, MBM * rb);
     const rsrc_t rw_ = make_rsrc(g.wc + n0 * (int64_t)rb, MBN * rb);
     const int sop = t >> 8, sr = t & 255;
     const rsrc_t rs_ = make_rsrc(sop ? g.ws + n0 * (int64_t)sb : g.as + m0 * (int64_t)sb, MBM * sb);
-    uint32_t go[2];
-    int lo[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = t + q * 512, r = i >> 2, c = i & 3;
-        go[q] = r * rb + c * 16;
-        lo[q] = pcode_off(r, c);
-    }
+    // thread t moves chunk t % 8 of rows t / 8 + 64 q, q < 4: one vector
+    // offset, the row step 64 q in the scalar offset (and the same LDS
+    // swizzle for the four rows: f(r + 64 q) = f(r))
+    const uint32_t go0 = (uint32_t)(t >> 3) * rb + (uint32_t)(t & 7) * 16;
+    const int lo0 = qcode_off(t >> 3, t & 7);
     const uint32_t gso = sr * sb;
-    const int slo = PSC + sop * (MBM * 16) + sr * 16;
-    auto load_regs = [&](MxRegs &R, int kt) __attribute__((always_inline)) {
-        const int o = kt * PKB;
-        R.a0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra_, go[0], o, 0));
-        R.a1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra_, go[1], o, 0));
-        R.w0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw_, go[0], o, 0));
-        R.w1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw_, go[1], o, 0));
+    const int slo = QSC + sop * (MBM * 16) + sr * 16;
+    struct QRegs {
+        u32x4_t a[4], w[4];
     };
-    auto store_regs = [&](const MxRegs &R, int b) __attribute__((always_inline)) {
-        *reinterpret_cast<u32x4_t *>(smem + b * PCODE + lo[0]) = R.a0;
-        *reinterpret_cast<u32x4_t *>(smem + b * PCODE + lo[1]) = R.a1;
-        *reinterpret_cast<u32x4_t *>(smem + PW + b * PCODE + lo[0]) = R.w0;
-        *reinterpret_cast<u32x4_t *>(smem + PW + b * PCODE + lo[1]) = R.w1;
+    auto load_regs = [&](QRegs &R, int kt) __attribute__((always_inline)) {
+        const int o = kt * QKB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int so = o + q * 64 * (int)rb;
+            R.a[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra_, go0, so, 0));
+            R.w[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw_, go0, so, 0));
+        }
+    };
+    auto store_regs = [&](const QRegs &R, int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<u32x4_t *>(smem + b * QCODE + lo0 + q * 64 * QKB) = R.a[q];
+            *reinterpret_cast<u32x4_t *>(smem + QW + b * QCODE + lo0 + q * 64 * QKB) = R.w[q];
+        }
     };
     auto load_scales = [&](int grp) __attribute__((always_inline)) {
         return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_, gso, grp * 16, 0));
     };
     auto store_scales = [&](u32x4_t v, int gb) __attribute__((always_inline)) {
-        *reinterpret_cast<u32x4_t *>(smem + slo + gb * PSG) = v;
+        *reinterpret_cast<u32x4_t *>(smem + slo + gb * QSG) = v;
     };
 
-    // fragment and scale addresses of this lane: fragment i of A is 32 i rows
-    // further (same swizzle), the second k64 sub-step two chunks further
     const int ra = wm * MWM + (lane & 31), rw = wn * MWN + (lane & 31);
-    const uint8_t *fa0 = smem + pcode_off(ra, lane >> 5), *fa1 = smem + (pcode_off(ra, lane >> 5) ^ 32);
-    const uint8_t *fb0 = smem + PW + pcode_off(rw, lane >> 5), *fb1 = smem + PW + (pcode_off(rw, lane >> 5) ^ 32);
-    const uint8_t *sca = smem + PSC + ra * 16, *scw = smem + PSC + MBM * 16 + rw * 16;
-    const int sh = 8 * (lane >> 5);  // upper half-wave: the odd 32-block of each k64
+    const int fa_off = qcode_off(ra, lane >> 5), fb_off = QW + qcode_off(rw, lane >> 5);
+    const uint8_t *sca = smem + QSC + ra * 16, *scw = smem + QSC + MBM * 16 + rw * 16;
+    const int sh = 8 * (lane >> 5);
+    // sub-step ks of stage b: chunk 2 ks + lane / 32, i.e. the ks = 0 offset ^ (32 ks)
     auto read_frags = [&](int b, int ks, uint4 *fa, uint4 *fb) __attribute__((always_inline)) {
-        const uint8_t *pa = (ks ? fa1 : fa0) + b * PCODE, *pb = (ks ? fb1 : fb0) + b * PCODE;
+        const uint8_t *pa = smem + b * QCODE + (fa_off ^ (ks << 5));
+        const uint8_t *pb = smem + b * QCODE + (fb_off ^ (ks << 5));
 #pragma unroll
-        for (int i = 0; i < MTM; ++i) fa[i] = *reinterpret_cast<const uint4 *>(pa + i * 32 * PKB);
+        for (int i = 0; i < MTM; ++i) fa[i] = *reinterpret_cast<const uint4 *>(pa + i * 32 * QKB);
 #pragma unroll
-        for (int j = 0; j < MTN; ++j) fb[j] = *reinterpret_cast<const uint4 *>(pb + j * 32 * PKB);
+        for (int j = 0; j < MTN; ++j) fb[j] = *reinterpret_cast<const uint4 *>(pb + j * 32 * QKB);
     };
-    // step kt's scale words (word kt % 4 of the group's 16 bytes) as stored;
-    // shifted for the lane when the step starts, so the reads have a sub-step
-    // of MFMAs to land
-    auto read_scales = [&](int kt, uint32_t *sa, uint32_t *sw) __attribute__((always_inline)) {
-        const int o = ((kt >> 2) & 1) * PSG + (kt & 3) * 4;
+    // step kt's 8 scale bytes per row (bytes 8 (kt % 2) .. of the group's 16)
+    auto read_scales = [&](int kt, u32x2_t *sa, u32x2_t *sw) __attribute__((always_inline)) {
+        const int o = ((kt >> 1) & 1) * QSG + (kt & 1) * 8;
 #pragma unroll
-        for (int i = 0; i < MTM; ++i) sa[i] = *reinterpret_cast<const uint32_t *>(sca + o + i * 32 * 16);
+        for (int i = 0; i < MTM; ++i) sa[i] = *reinterpret_cast<const u32x2_t *>(sca + o + i * 32 * 16);
 #pragma unroll
-        for (int j = 0; j < MTN; ++j) sw[j] = *reinterpret_cast<const uint32_t *>(scw + o + j * 32 * 16);
+        for (int j = 0; j < MTN; ++j) sw[j] = *reinterpret_cast<const u32x2_t *>(scw + o + j * 32 * 16);
     };
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
@@ -252,60 +246,57 @@ __device__ __forceinline__ void mx_tile_pipe(const MxArgs &g, uint8_t *smem, int
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     uint4 fa[2][MTM], fb[2][MTN];
-    uint32_t sa[2][MTM], sw[2][MTN];
-    MxRegs R0, R1;  // named (not an array), so they stay in registers
-    u32x4_t RS;     // the next scale group
+    u32x2_t sa[MTM], sw[MTN];
+    QRegs R;
+    u32x4_t RS;
 
-    // Every step loads codes two steps ahead (past the end, a repeat of the
-    // last step) and stores one step, so the steps are straight-line code;
-    // the third step of a group loads the next group's scales, the fourth
-    // stores them.
-    load_regs(R0, 0);
-    store_regs(R0, 0);
+    load_regs(R, 0);
     store_scales(load_scales(0), 0);
-    load_regs(R1, min(1, KT - 1));
+    store_regs(R, 0);
     lds_barrier();
     read_frags(0, 0, fa[0], fb[0]);
-    read_scales(0, sa[0], sw[0]);
+    read_scales(0, sa, sw);
 
-    // step kt = 4 j + u on code stage b = u % 2 (constants in each unrolled copy)
     auto step = [&](int kt, auto uc) __attribute__((always_inline)) {
-        constexpr int u = decltype(uc)::value, b = u & 1;
-        uint32_t ssa[MTM], ssw[MTN];
+        constexpr int u = decltype(uc)::value, b = u;
+        uint32_t s0a[MTM], s0w[MTN], s1a[MTM], s1w[MTN];
 #pragma unroll
-        for (int i = 0; i < MTM; ++i) ssa[i] = sa[b][i] >> sh;
+        for (int i = 0; i < MTM; ++i) {
+            s0a[i] = sa[i].x >> sh;
+            s1a[i] = sa[i].y >> sh;
+        }
 #pragma unroll
-        for (int j = 0; j < MTN; ++j) ssw[j] = sw[b][j] >> sh;
-        // R0 / R1 alternate: the free one loads step kt + 2, the other holds kt + 1
-        if constexpr (b == 0)
-            load_regs(R0, min(kt + 2, KT - 1));
-        else
-            load_regs(R1, min(kt + 2, KT - 1));
-        if constexpr (u == 2) RS = load_scales(min((kt >> 2) + 1, (KT >> 2) - 1));
+        for (int j = 0; j < MTN; ++j) {
+            s0w[j] = sw[j].x >> sh;
+            s1w[j] = sw[j].y >> sh;
+        }
+        load_regs(R, min(kt + 1, KT - 1));
+        if constexpr (u == 0) RS = load_scales(min((kt >> 1) + 1, (KT >> 1) - 1));
         read_frags(b, 1, fa[1], fb[1]);
-        // the schedule is kept as written: reads ahead of the MFMAs that
-        // cover them, nothing moved across the phases (registers)
         __builtin_amdgcn_sched_barrier(0);
-        mx_mfmas(acc, fa[0], fb[0], ssa, ssw, 0);
+        mx_mfmas(acc, fa[0], fb[0], s0a, s0w, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (b == 0)
-            store_regs(R1, 1);
-        else
-            store_regs(R0, 0);
-        if constexpr (u == 3) store_scales(RS, ((kt >> 2) + 1) & 1);
+        read_frags(b, 2, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfmas(acc, fa[1], fb[1], s0a, s0w, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(b, 3, fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfmas(acc, fa[0], fb[0], s1a, s1w, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        store_regs(R, b ^ 1);
+        if constexpr (u == 1) store_scales(RS, ((kt >> 1) + 1) & 1);
         lds_barrier();
-        // (after the last step these read stages nobody uses)
+        // (after the last step these read a stage nobody uses)
         read_frags(b ^ 1, 0, fa[0], fb[0]);
-        read_scales(kt + 1, sa[b ^ 1], sw[b ^ 1]);
+        read_scales(kt + 1, sa, sw);
         __builtin_amdgcn_sched_barrier(0);
-        mx_mfmas(acc, fa[1], fb[1], ssa, ssw, 1);
+        mx_mfmas(acc, fa[1], fb[1], s1a, s1w, 1);
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int kt = 0; kt < KT; kt += 4) {
+    for (int kt = 0; kt < KT; kt += 2) {
         step(kt, std::integral_constant<int, 0>());
         step(kt + 1, std::integral_constant<int, 1>());
-        step(kt + 2, std::integral_constant<int, 2>());
-        step(kt + 3, std::integral_constant<int, 3>());
     }
     mx_store<kOutBf16>(g, acc, m0, n0, smem);
 }
@@ -422,7 +413,7 @@ __global__ __launch_bounds__(MNT, 1) void mx_gemm_kernel(MxArgs g) {
     // resource with 32-bit offsets (256 * K / 2 bytes < 2^31: K < 2^24);
     // longer rows take the staged loop, which indexes in 64 bits
     if (m0 + MBM <= g.M && n0 + MBN <= g.N && (g.K & 511) == 0 && g.K < kMxPipeMaxK)
-        mx_tile_pipe<kOutBf16>(g, smem, m0, n0);
+        mx_tile_pipe256<kOutBf16>(g, smem, m0, n0);
     else
         mx_tile_staged<kOutBf16>(g, smem, m0, n0);
 }
@@ -432,7 +423,7 @@ hipError_t launch_mx(const MxArgs &g, hipStream_t s) {
     const int64_t nb = ((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN);
     if (nb <= 0) return hipSuccess;
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const size_t lds = 2 * (size_t)STAGE;
+    const size_t lds = 2 * (size_t)STAGE > (size_t)QLDS ? 2 * (size_t)STAGE : (size_t)QLDS;
     static std::atomic<uint32_t> attr_done{0};
     if (hipError_t e = set_dyn_lds_once(attr_done, (const void *)mx_gemm_kernel<kOutBf16>, (int)lds); e != hipSuccess)
         return e;
