@@ -636,6 +636,9 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
     if (kind == DECODE_BF16) {
         if (M <= 4) return {1, 16, 1, 1};
         if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1};
+        // wide layers at batch 33-64: 128-column strips read the batch once
+        // per 128 columns instead of per 64 (gate_up at batch 64: 77.9 -> 69.8 us)
+        if (M > 32 && N >= 16384) return {8, 4, 1, 1};
         const int ng = N >= 6144 || M > 32 ? 4 : 2;
         const int64_t nb = (N + 16 * ng - 1) / (16 * ng);
         const int s = nb <= 64 ? 4 : 2;
@@ -664,6 +667,7 @@ int plan_slices(const DecodePlan &p, int64_t M, int64_t N, void *ws, size_t ws_b
 template <int MG>
 hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
                           int out_type, int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s) {
+    if (p.ng == 8) return launch_bf16_cfg<MG, 8, 4, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 2) return launch_bf16_cfg<MG, 2, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);

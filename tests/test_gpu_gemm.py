@@ -266,7 +266,9 @@ def _bf16(nv, a, wt, od):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (1, 4096, 4096), (8, 300, 136), (17, 64, 512), (64, 1000, 1032),
-                                   (65, 129, 264), (300, 520, 1024)])
+                                   (65, 129, 264), (300, 520, 1024),
+                                   # batch 33-64 on a wide layer: 128-column decode strips, the last one partial
+                                   (40, 16400, 520), (64, 16384, 4096)])
 def test_bf16_gemm_shapes(nv, oracle_mod, M, N, K):
     g = np.random.default_rng(M * 3 + N + K)
     a = wl.to_bf16_bits(g.standard_normal((M, K), dtype=np.float32))
