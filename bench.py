@@ -537,7 +537,9 @@ def _decode(nv, wl, layers, s, e):
         qa = [(torch.empty(1, dtype=torch.float32, device=dev),
                torch.empty(max(nv.quant_gemm_workspace_size(Md, L["N"], L["K"]), 16), dtype=torch.uint8,
                            device=dev)) for L in layers]
-        fused = [Md * L["K"] <= 196608 and Md <= 2 for L in layers]
+        # the library's route (include/nvfp4.h, nvfp4_quant_gemm): which layers quantize in the decode kernel
+        fused = [L["K"] % 32 == 0 and Md * L["K"] <= 196608 and
+                 (Md <= 2 or (Md <= 8 and L["N"] <= 8192 and Md * L["K"] <= 32768)) for L in layers]
 
         def dec4_step(c):
             for i, L in enumerate(layers):

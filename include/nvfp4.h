@@ -167,9 +167,11 @@ size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   exit); dynamic alpha needs at least nvfp4_quantize_workspace_size(M, K)
  *   bytes (NVFP4_EWORKSPACE otherwise).
  * Paths, by shape and workspace:
- *   - M <= 2, M * K <= 196608, K % 32 == 0: one decode kernel quantizes the
- *     batch into LDS in every workgroup (each forms the dynamic alpha itself)
- *     and streams the weights (larger batches measured faster quantized once);
+ *   - K % 32 == 0 and either M <= 2 with M * K <= 196608, or M <= 8 with
+ *     N <= 8192 and M * K <= 32768: one decode kernel quantizes the batch
+ *     into LDS in every workgroup (each forms the dynamic alpha itself) and
+ *     streams the weights (larger batches, and wider layers, measured faster
+ *     quantized once);
  *   - otherwise, with nvfp4_quant_gemm_workspace_size(M, N, K) bytes: the
  *     quantizer writes codes and scales into the workspace and nvfp4_gemm's
  *     kernels run on them (one quantization per activation element; the

@@ -70,9 +70,7 @@ QgLayout qg_layout(int64_t M, int64_t N, int64_t K, bool dyn) {
     return l;
 }
 
-bool fused_decode_shape(int64_t M, int64_t K) {
-    return M <= nvfp4::kFusedDecodeMaxM && M * K <= nvfp4::kFusedDecodeMaxElems && K % 32 == 0;
-}
+bool fused_decode_shape(int64_t M, int64_t N, int64_t K) { return nvfp4::fused_decode_route(M, N, K); }
 
 bool decode_shape(int64_t M, int64_t K, int kmult) {
     return M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % kmult == 0;
@@ -202,7 +200,7 @@ int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const 
 size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     const size_t parts = nvfp4_quantize_workspace_size(M, K);  // the minimum with a dynamic alpha
-    if (fused_decode_shape(M, K)) {
+    if (fused_decode_shape(M, N, K)) {
         const size_t split = nvfp4::decode_workspace_bytes(nvfp4::DECODE_FUSED, M, N, K);
         return split > parts ? split : parts;
     }
@@ -236,7 +234,7 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
     }
     if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     // decode batches: one kernel quantizes the batch into LDS and runs the decode GEMM
-    if (fused_decode_shape(M, K))
+    if (fused_decode_shape(M, N, K))
         return hip_status(nvfp4::launch_skinny_fused((const uint16_t *)x_bf16, ld_x, a_alpha, dyn, w_codes, w_scales,
                                                      w_alpha, M, N, K, out, out_dtype, ld_out, workspace,
                                                      workspace_bytes, s),

@@ -105,11 +105,23 @@ hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, 
                                int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
                                size_t ws_bytes, hipStream_t s);
 
-// nvfp4_quant_gemm routes M <= kFusedDecodeMaxM with M * K <=
-// kFusedDecodeMaxElems (108 KB of codes and scales in LDS: every Qwen3-8B
-// layer at 16 tokens) to the fused decode kernel.
+// nvfp4_quant_gemm routes to the fused decode kernel batches of at most
+// kFusedDecodeMaxM rows with M * K <= kFusedDecodeMaxElems (108 KB of codes
+// and scales in LDS: every Qwen3-8B layer at 16 tokens), and batches of at
+// most kFusedDecodeWideM rows on layers of at most kFusedDecodeWideN
+// columns whose batch fits a workgroup's registers (M * K <=
+// kFusedDecodeRegElems): there the per-workgroup quantization costs less
+// than a separate quantizer launch (measured at batch 4 and 8 on the
+// Qwen3-8B qkv and o projections), while wide layers repeat it too often.
 constexpr int64_t kFusedDecodeMaxM = 2;
 constexpr int64_t kFusedDecodeMaxElems = 16 * 12288;
+constexpr int64_t kFusedDecodeWideM = 8;
+constexpr int64_t kFusedDecodeWideN = 8192;
+constexpr int64_t kFusedDecodeRegElems = 32768;
+inline bool fused_decode_route(int64_t M, int64_t N, int64_t K) {
+    if (K % 32 != 0 || M * K > kFusedDecodeMaxElems) return false;
+    return M <= kFusedDecodeMaxM || (M <= kFusedDecodeWideM && N <= kFusedDecodeWideN && M * K <= kFusedDecodeRegElems);
+}
 
 // Largest M routed to the skinny decode kernels by bf16_gemm and nvfp4_gemm.
 constexpr int64_t kSkinnyMaxM = 64;

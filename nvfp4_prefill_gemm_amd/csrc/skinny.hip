@@ -420,10 +420,12 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
                 if ((oc & 1) == 0) lsw[r * sb + (oc >> 1)] = (uint8_t)code;
             }
         };
-        constexpr uint32_t NT = WAVES * 64, kRegOcts = 4;
+        // batches of 3-8 rows (FP16 form) hold up to eight octets per thread;
+        // the FP4 form (one or two rows) needs at most four
+        constexpr uint32_t NT = WAVES * 64, kRegOcts = kF4 ? 4 : 8;
         const bool whole = cs == 0 && (uint32_t)ce * 16u >= octs;
         if (whole && total <= kRegOcts * NT) {
-            // the batch fits in registers (up to four octets per thread): one
+            // the batch fits in registers (kRegOcts octets per thread): one
             // load, the amax, then quantization from the same registers
             uint4 v[kRegOcts];
 #pragma unroll
