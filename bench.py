@@ -407,7 +407,8 @@ def _fused(nv, layers, sets, M, flops_step, reps, s, e):
 
 def _quant_out(nv, layers, M, flops_step, reps, s, e):
     """NVFP4 GEMM whose epilogue quantizes Y to NVFP4 for the next layer
-    (static output scale), same layers and activations."""
+    (static output scale), and the same with a dynamic output scale; same
+    layers and activations."""
     import torch
 
     dev = torch.device("cuda", 0)
@@ -428,7 +429,25 @@ def _quant_out(nv, layers, M, flops_step, reps, s, e):
     e.record()
     torch.cuda.synchronize()
     out["quant_out_gemm_tflops"] = round(flops_step / (s.elapsed_time(e) / reps * 1e-3) / 1e12, 2)
-    del yq
+    # the same with the output tensor scale from Y's own amax (FP32 Y through
+    # a workspace, then the FP32 quantizer)
+    ya = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(nv.gemm_quant_out_dynamic_workspace_size(M, L["N"], L["K"]) for L in layers),
+                     dtype=torch.uint8, device=dev)
+
+    def qd_step():
+        for L, (yc, ysc) in zip(layers, yq):
+            nv.nvfp4_gemm_quant_out_dynamic(L["ac"], L["asc"], L["aal"], L["wc"], L["ws"], L["wa"], yc, ysc, ya, ws)
+    for _ in range(2):
+        qd_step()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        qd_step()
+    e.record()
+    torch.cuda.synchronize()
+    out["quant_out_dynamic_gemm_tflops"] = round(flops_step / (s.elapsed_time(e) / reps * 1e-3) / 1e12, 2)
+    del yq, ws
     return out
 
 

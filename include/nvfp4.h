@@ -144,13 +144,38 @@ int nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_a
  *   y_alpha float[1] in (device): the output tensor scale, e.g. calibrated.
  *   N % 16 == 0, K % 16 == 0; operands as in nvfp4_gemm.  The codes equal
  *   those the quantizer gives for the FP32 output of the same product.
- * A dynamic output scale would need the whole output's amax before any
- * block is quantized, so it is not offered here.
+ * A dynamic output scale needs the whole output's amax before any block is
+ * encoded, so the epilogue cannot apply it: nvfp4_gemm_quant_out_dynamic
+ * below forms Y first.
  */
 int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                          const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
                          int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales, const float *y_alpha,
                          void *stream);
+
+/*
+ * nvfp4_gemm_quant_out with a dynamic output tensor scale (Mix-Quant Section
+ * 3.3, Eq. 2 and Eq. 3 on the product Y, the tensor scale taken from Y's
+ * largest magnitude): alpha_Y = fl32(max |y| / 2688) over every FP32 output
+ * y = (acc * alpha_A) * alpha_W (the values nvfp4_gemm's tile kernel gives
+ * with an FP32 output), then codes and scales of Y as in
+ * nvfp4_gemm_quant_out with that alpha.  The whole Y must be formed before
+ * any block is encoded, so the call runs three kernels on the stream: the
+ * tile GEMM writing Y in FP32 to the workspace with per-wave maxima of |y|,
+ * a one-workgroup reduction to alpha_Y, and an FP32 quantizer.
+ *   operands and N, K as in nvfp4_gemm_quant_out
+ *   y_alpha float[1] device, written
+ *   workspace: 256-byte aligned device scratch of at least
+ *   nvfp4_gemm_quant_out_dynamic_workspace_size(M, N, K) bytes (the FP32 Y
+ *   and the maxima; contents undefined on entry and exit), else
+ *   NVFP4_EWORKSPACE.
+ * K == 0 gives alpha_Y = 0 and zero codes and scales.
+ */
+size_t nvfp4_gemm_quant_out_dynamic_workspace_size(int64_t M, int64_t N, int64_t K);
+int nvfp4_gemm_quant_out_dynamic(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                                 const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                 int64_t M, int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales,
+                                 float *y_alpha, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace nvfp4_quant_gemm uses at these sizes for its
  * fastest path (see nvfp4_quant_gemm). */

@@ -31,6 +31,8 @@ _SIGNATURES = {
     "nvfp4_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "nvfp4_gemm_quant_out": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_gemm_quant_out_dynamic_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_gemm_quant_out_dynamic": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quant_gemm": (_I, [_P, _I64, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "bf16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -300,6 +302,44 @@ def nvfp4_gemm_quant_out(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha,
                                     _stream(stream))
     _check("nvfp4_gemm_quant_out", rc)
     return y_codes, y_scales
+
+
+def gemm_quant_out_dynamic_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_gemm_quant_out_dynamic_workspace_size(M, N, K))
+
+
+def nvfp4_gemm_quant_out_dynamic(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha,
+                                 y_codes: torch.Tensor | None = None, y_scales: torch.Tensor | None = None,
+                                 y_alpha: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                 stream=None):
+    """NVFP4 GEMM with an NVFP4 output whose tensor scale comes from the
+    output's own amax.  Returns (y_codes uint8 [M, N/2], y_scales uint8
+    [M, N/16], y_alpha float32 [1])."""
+    M, N, K = _nvfp4_operands(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha)
+    if N % 16:
+        raise ValueError(f"N = {N} must be a multiple of 16 for an NVFP4 output")
+    dev = a_codes.device
+    if y_codes is None:
+        y_codes = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    if y_scales is None:
+        y_scales = torch.empty((M, N // 16), dtype=torch.uint8, device=dev)
+    if y_alpha is None:
+        y_alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    _mat(y_codes, "y_codes", torch.uint8, M, N // 2)
+    _mat(y_scales, "y_scales", torch.uint8, M, N // 16)
+    _alpha(y_alpha, "y_alpha")
+    if workspace is None:
+        workspace = torch.empty(max(gemm_quant_out_dynamic_workspace_size(M, N, K), 256), dtype=torch.uint8,
+                                device=dev)
+    _tensor(workspace, "workspace")
+    _same_device(("a_codes", a_codes), ("a_scales", a_scales), ("a_alpha", a_alpha), ("w_codes", w_codes),
+                 ("w_scales", w_scales), ("w_alpha", w_alpha), ("y_alpha", y_alpha), ("y_codes", y_codes),
+                 ("y_scales", y_scales), ("workspace", workspace))
+    rc = lib().nvfp4_gemm_quant_out_dynamic(_ptr(a_codes), _ptr(a_scales), _ptr(a_alpha), _ptr(w_codes),
+                                            _ptr(w_scales), _ptr(w_alpha), M, N, K, _ptr(y_codes), _ptr(y_scales),
+                                            _ptr(y_alpha), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("nvfp4_gemm_quant_out_dynamic", rc)
+    return y_codes, y_scales, y_alpha
 
 
 def quant_gemm_workspace_size(M: int, N: int, K: int) -> int:

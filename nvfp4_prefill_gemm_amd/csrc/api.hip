@@ -197,6 +197,52 @@ int nvfp4_gemm_quant_out(const uint8_t *a_codes, const uint8_t *a_scales, const 
                       "nvfp4 gemm kernel (quantized output)");
 }
 
+size_t nvfp4_gemm_quant_out_dynamic_workspace_size(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    if (M <= 0 || N <= 0) return 0;
+    return align256((size_t)M * (size_t)N * sizeof(float)) +
+           align256((size_t)nvfp4::gemm_amax_parts_bound(M, N) * sizeof(uint32_t));
+}
+
+int nvfp4_gemm_quant_out_dynamic(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                                 const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
+                                 int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales, float *y_alpha,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "nvfp4_gemm_quant_out_dynamic";
+    if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (K % 16 != 0) return fail(NVFP4_EINVAL, "%s: K (%lld) must be a multiple of 16", fn, (long long)K);
+    if (N % 16 != 0) return fail(NVFP4_EINVAL, "%s: N (%lld) must be a multiple of 16", fn, (long long)N);
+    if (M == 0 || N == 0) return ok();
+    if (!y_codes || !y_scales || !y_alpha) return fail(NVFP4_EINVAL, "%s: null output pointer", fn);
+    if (!aligned(y_codes, 4)) return fail(NVFP4_EINVAL, "%s: y_codes must be 4-byte aligned", fn);
+    if (!aligned(y_alpha, 4)) return fail(NVFP4_EINVAL, "%s: y_alpha is misaligned", fn);
+    hipStream_t s = as_stream(stream);
+    int rc;
+    if (K == 0) {  // Y = 0: alpha 0, zero codes and zero scales
+        if ((rc = hip_status(nvfp4::launch_fill_zero(y_alpha, 1, 1, 1, 4, s), "fill kernel"))) return rc;
+        if ((rc = hip_status(nvfp4::launch_fill_zero(y_codes, M, N / 2, N / 2, 1, s), "fill kernel"))) return rc;
+        return hip_status(nvfp4::launch_fill_zero(y_scales, M, N / 16, N / 16, 1, s), "fill kernel");
+    }
+    if ((rc = check_nvfp4(a_codes, a_scales, a_alpha, "A", fn))) return rc;
+    if ((rc = check_nvfp4(w_codes, w_scales, w_alpha, "W", fn))) return rc;
+    const size_t need = nvfp4_gemm_quant_out_dynamic_workspace_size(M, N, K);
+    if (!workspace || workspace_bytes < need)
+        return fail(NVFP4_EWORKSPACE, "%s: needs %zu bytes of workspace, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(NVFP4_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+    const int64_t nparts = nvfp4::gemm_amax_parts(M, N);
+    if (nparts > 0x7FFFFFFF) return fail(NVFP4_EUNSUPPORTED, "%s: too many output tiles", fn);
+    float *y = (float *)workspace;
+    uint32_t *parts = (uint32_t *)((char *)workspace + align256((size_t)M * (size_t)N * sizeof(float)));
+    if ((rc = hip_status(nvfp4::launch_gemm_nvfp4_f32_amax(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M,
+                                                           N, K, y, parts, s),
+                         "nvfp4 gemm kernel (FP32 output and amax)")))
+        return rc;
+    if ((rc = hip_status(nvfp4::launch_alpha_from_partials(parts, (int)nparts, y_alpha, s), "alpha kernel")))
+        return rc;
+    return hip_status(nvfp4::launch_quantize_f32(y, M, N, N, y_codes, y_scales, y_alpha, s), "FP32 quantize kernel");
+}
+
 size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     const size_t parts = nvfp4_quantize_workspace_size(M, K);  // the minimum with a dynamic alpha

@@ -82,6 +82,7 @@ struct GemmArgs {
     int64_t ld_out;
     uint8_t *out_scales;      // NVFP4 output: E4M3 block scales [M, N/16]
     const float *out_alpha;   // NVFP4 output: static tensor scale
+    uint32_t *amax_part = nullptr;  // OUT_F32_AMAX: 8 slots per workgroup
     int rows_rsrc = 0;        // edge tiles may address a tile's rows through one buffer resource (< 2^31 bytes)
     bool vec = false;         // FP32/BF16 output: out and ld_out allow 16-byte stores
 };
@@ -694,6 +695,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t
         float *slab = reinterpret_cast<float *>(lds) + wave * epilogue_slab_floats<TN>();
         store_acc_tiles<TM, TN, kOut == OUT_BF16>(acc, sa, sw, slab, g.out, g.ld_out, m0 + wm * C::WM,
                                                   n0 + wn * C::WN, g.M, g.N, g.vec);
+        if constexpr (kOut == OUT_F32_AMAX) {
+            // max |y| over the wave tile, each y formed as it was stored
+            // (elements past the M or N edge are exact zeros)
+            static_assert(NT / 64 <= 8, "eight slots per workgroup");
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        m = max(m, __float_as_uint((acc[i][j][r] * sa) * sw) & 0x7FFFFFFFu);
+            for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+            if (lane == 0) {
+                g.amax_part[(int64_t)blockIdx.x * 8 + wave] = m;
+                if (NT / 64 == 4) g.amax_part[(int64_t)blockIdx.x * 8 + 4 + wave] = 0u;
+            }
+        }
     }
 }
 
@@ -733,7 +752,7 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     GemmArgs ga = g;
     const int64_t a_row = kKind == KIND_NVFP4 ? g.K / 2 : g.lda * 2, w_row = kKind == KIND_BF16 ? g.K * 2 : g.K / 2;
     ga.rows_rsrc = C::BM * a_row < (int64_t(1) << 31) && C::BN * w_row < (int64_t(1) << 31);
-    ga.vec = kOut != OUT_NVFP4 && epilogue_vec_ok(g.out, g.ld_out, kOut == OUT_F32 ? 4 : 2);
+    ga.vec = kOut != OUT_NVFP4 && epilogue_vec_ok(g.out, g.ld_out, kOut == OUT_BF16 ? 2 : 4);
     static std::atomic<uint32_t> attr_done{0};
     if (hipError_t e = set_dyn_lds_once(attr_done, (const void *)kern, (int)lds_bytes); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds_bytes, s, ga);
@@ -754,16 +773,23 @@ int tile_override() {
 
 template <class C, int kKind>
 hipError_t launch_out(const GemmArgs &g, int out_type, hipStream_t s) {
-    if constexpr (kKind == KIND_NVFP4)
+    if constexpr (kKind == KIND_NVFP4) {
         if (out_type == OUT_NVFP4) return launch_cfg<C, kKind, OUT_NVFP4>(g, s);
-    if (out_type == OUT_NVFP4) return hipErrorInvalidValue;
+        if (out_type == OUT_F32_AMAX) return launch_cfg<C, kKind, OUT_F32_AMAX>(g, s);
+    }
+    if (out_type == OUT_NVFP4 || out_type == OUT_F32_AMAX) return hipErrorInvalidValue;
     return out_type == OUT_BF16 ? launch_cfg<C, kKind, OUT_BF16>(g, s) : launch_cfg<C, kKind, OUT_F32>(g, s);
+}
+
+// Tile choice: 1 = 4-wave 256 x 256, 2 = 8-wave 256 x 256, 3 = 128 x 128.
+int tile_choice(int64_t M, int64_t N) {
+    const int t = tile_override();
+    return t ? t : ((M + 255) / 256) * ((N + 255) / 256) >= 256 ? 2 : 3;
 }
 
 template <int kKind>
 hipError_t launch(const GemmArgs &g, int out_type, hipStream_t s) {
-    int t = tile_override();
-    if (t == 0) t = ((g.M + 255) / 256) * ((g.N + 255) / 256) >= 256 ? 2 : 3;
+    int t = tile_choice(g.M, g.N);
     // the fused prologue needs more registers than 8 waves leave the main
     // loop (it spills there): the 4-wave 256 x 256 tile (512 registers per
     // lane) runs it (an explicit NVFP4_GEMM_TILE=big8 still takes 8 waves)
@@ -789,6 +815,21 @@ hipError_t launch_gemm_nvfp4_quant_out(const uint8_t *a_codes, const uint8_t *a_
     GemmArgs g{a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, 0, y_codes, N / 2, y_scales, y_alpha};
     return launch<KIND_NVFP4>(g, OUT_NVFP4, s);
 }
+
+hipError_t launch_gemm_nvfp4_f32_amax(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                                      const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                      int64_t M, int64_t N, int64_t K, float *y, uint32_t *parts, hipStream_t s) {
+    GemmArgs g{a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, 0, y, N, nullptr, nullptr};
+    g.amax_part = parts;
+    return launch<KIND_NVFP4>(g, OUT_F32_AMAX, s);
+}
+
+int64_t gemm_amax_parts(int64_t M, int64_t N) {
+    const int64_t b = tile_choice(M, N) == 3 ? 128 : 256;
+    return ((M + b - 1) / b) * ((N + b - 1) / b) * 8;
+}
+
+int64_t gemm_amax_parts_bound(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128) * 8; }
 
 hipError_t launch_gemm_fused(const uint16_t *x, int64_t ld_x, const float *a_alpha, const uint8_t *w_codes,
                              const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K,

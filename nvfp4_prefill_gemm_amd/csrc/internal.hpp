@@ -48,7 +48,9 @@ hipError_t quantize_scratch(uint32_t **ptr, size_t *bytes);
 // alpha from partials only (fused path, dynamic mode).
 hipError_t launch_alpha_from_partials(const uint32_t *partials, int nparts, float *alpha, hipStream_t s);
 
-enum OutType { OUT_F32 = 0, OUT_BF16 = 1, OUT_NVFP4 = 2 };
+// OUT_F32_AMAX: FP32 output plus, per workgroup, eight slots of the waves'
+// max |y| (FP32 bits; unused slots 0) for a dynamic output tensor scale.
+enum OutType { OUT_F32 = 0, OUT_BF16 = 1, OUT_NVFP4 = 2, OUT_F32_AMAX = 3 };
 
 hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                              const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
@@ -61,6 +63,22 @@ hipError_t launch_gemm_nvfp4_quant_out(const uint8_t *a_codes, const uint8_t *a_
                                        const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                                        int64_t M, int64_t N, int64_t K, uint8_t *y_codes, uint8_t *y_scales,
                                        const float *y_alpha, hipStream_t s);
+
+// Tile GEMM with FP32 output y [M, N] (row stride N) and the per-wave maxima
+// of |y| in `parts` (gemm_amax_parts(M, N) slots).
+hipError_t launch_gemm_nvfp4_f32_amax(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                                      const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                      int64_t M, int64_t N, int64_t K, float *y, uint32_t *parts, hipStream_t s);
+// Slots launch_gemm_nvfp4_f32_amax writes for this shape (8 per output
+// tile), and an upper bound over every tile choice.
+int64_t gemm_amax_parts(int64_t M, int64_t N);
+int64_t gemm_amax_parts_bound(int64_t M, int64_t N);
+
+// Eq. 3 / Eq. 2 on an FP32 tensor y [rows, ld] (cols % 16 == 0) with the
+// tensor scale *alpha (device pointer): codes [rows, cols/2] (4-byte
+// aligned), scales [rows, cols/16].
+hipError_t launch_quantize_f32(const float *y, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                               uint8_t *scales, const float *alpha, hipStream_t s);
 
 hipError_t launch_gemm_fused(const uint16_t *x, int64_t ld_x, const float *a_alpha,
                              const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,

@@ -341,6 +341,98 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_
     return hipGetLastError();
 }
 
+namespace {
+
+// Eq. 3 / Eq. 2 on FP32 values, each taken as it is (a GEMM output quantized
+// for the next layer): one 16-element block per lane and iteration, the tensor
+// scale read from device memory.  Eq. 3: s = RN(amax / t), t = RN(alpha * 6),
+// by Markstein's correction against one reciprocal of t where that is exact
+// (t in [2^-100, 2^100], amax zero or in [2^-100, t * 2^120]), else the IEEE
+// quotient; the hardware FP32 -> FP8 convert after the clamp to 448.  Eq. 2:
+// d = RN(alpha * sigma), each element's RN(y / d) by the corrected quotient
+// against RN(1/d) under the same conditions (and no nonzero |y| below
+// 2^-100), else the IEEE quotient; d == 0 gives signed zeros.  E2M1 by the
+// hardware FP32 -> FP4 convert (nearest-even, saturating, sign kept).
+__global__ __launch_bounds__(kThreads) void quantize_f32_kernel(const float *__restrict__ y, int64_t rows,
+                                                                int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
+                                                                uint8_t *__restrict__ scales,
+                                                                const float *__restrict__ alpha) {
+    const float ya = *alpha;
+    const float t6 = ya * kQmax, rt6 = t6 > 0.0f ? div_rn(1.0f, t6) : 0.0f;
+    const bool tfast = (t6 >= 0x1p-100f) & (t6 <= 0x1p100f);
+    const int64_t bpr = cols >> 4, nblk = rows * bpr;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = b / bpr, c = b - r * bpr;
+        const float4 *p = reinterpret_cast<const float4 *>(y + r * ld + c * 16);
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 t = p[e];
+            v[4 * e] = t.x;
+            v[4 * e + 1] = t.y;
+            v[4 * e + 2] = t.z;
+            v[4 * e + 3] = t.w;
+        }
+        uint32_t am = 0;
+        bool tiny = false;  // a nonzero |y| below 2^-100
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t ab = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+            am = max(am, ab);
+            tiny = tiny | ((ab != 0u) & (ab < 0x0D800000u));
+        }
+        const float amax = __uint_as_float(am);
+        float sq;
+        if (tfast & (amax <= t6 * 0x1p120f) & ((amax == 0.0f) | (amax >= 0x1p-100f))) {
+            const float q0 = amax * rt6;
+            sq = __builtin_fmaf(__builtin_fmaf(-q0, t6, amax), rt6, q0);
+        } else {
+            sq = t6 > 0.0f ? div_rn(amax, t6) : 0.0f;
+        }
+        const uint32_t code = e4m3_encode(sq);
+        const float d = ya * e4m3_decode(code);
+        const float rd = d > 0.0f ? div_rn(1.0f, d) : 0.0f;
+        float qv[16];
+        if ((d >= 0x1p-100f) & (d <= 0x1p100f) & !tiny & (amax <= d * 0x1p120f)) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float q0 = v[e] * rd;
+                qv[e] = __builtin_fmaf(__builtin_fmaf(-q0, d, v[e]), rd, q0);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                qv[e] = d > 0.0f ? div_rn(v[e], d) : __uint_as_float(__float_as_uint(v[e]) & 0x80000000u);
+        }
+        uint32_t w0 = 0, w1 = 0;
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[0], qv[1], 1.0f, 0);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[2], qv[3], 1.0f, 1);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[4], qv[5], 1.0f, 2);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, qv[6], qv[7], 1.0f, 3);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[8], qv[9], 1.0f, 0);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[10], qv[11], 1.0f, 1);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[12], qv[13], 1.0f, 2);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, qv[14], qv[15], 1.0f, 3);
+        uint32_t *cp = reinterpret_cast<uint32_t *>(codes + r * (cols >> 1) + c * 8);
+        cp[0] = w0;
+        cp[1] = w1;
+        scales[r * bpr + c] = (uint8_t)code;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_f32(const float *y, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                               uint8_t *scales, const float *alpha, hipStream_t s) {
+    const int64_t nblk = rows * (cols >> 4);
+    if (nblk <= 0) return hipSuccess;
+    int64_t g = (nblk + kThreads - 1) / kThreads;
+    if (g > 16384) g = 16384;
+    hipLaunchKernelGGL(quantize_f32_kernel, dim3((unsigned)g), dim3(kThreads), 0, s, y, rows, cols, ld, codes, scales,
+                       alpha);
+    return hipGetLastError();
+}
+
 hipError_t launch_alpha_from_partials(const uint32_t *partials, int nparts, float *alpha, hipStream_t s) {
     hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(kThreads), 0, s, partials, nparts, alpha);
     return hipGetLastError();

@@ -120,3 +120,20 @@ def test_gemm_argument_errors(L):
     assert b"workspace must be 16-byte aligned" in L.nvfp4_last_error()
     assert b(FAKE, FAKE, 8, 8, 16, FAKE, 0, 8, misaligned, 4096, None) == NVFP4_EINVAL
     assert b"workspace must be 16-byte aligned" in L.nvfp4_last_error()
+
+
+def test_quant_out_dynamic_argument_errors(L):
+    from nvfp4_prefill_gemm_amd.binding import NVFP4_EINVAL, NVFP4_EWORKSPACE
+
+    f = L.nvfp4_gemm_quant_out_dynamic
+    need = L.nvfp4_gemm_quant_out_dynamic_workspace_size(64, 256, 512)
+    assert need >= 64 * 256 * 4  # the FP32 product
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert f(*args, 64, 264, 512, FAKE, FAKE, FAKE, FAKE, need, None) == NVFP4_EINVAL  # N % 16
+    assert b"multiple of 16" in L.nvfp4_last_error()
+    assert f(*args, 64, 256, 520, FAKE, FAKE, FAKE, FAKE, need, None) == NVFP4_EINVAL  # K % 16
+    assert f(*args, 64, 256, 512, None, FAKE, FAKE, FAKE, need, None) == NVFP4_EINVAL  # null y_codes
+    assert f(*args, 64, 256, 512, FAKE, FAKE, FAKE, FAKE, need - 1, None) == NVFP4_EWORKSPACE
+    assert f(*args, 64, 256, 512, FAKE, FAKE, FAKE, None, 0, None) == NVFP4_EWORKSPACE
+    assert f(*args, 64, 256, 512, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1010), need, None) == NVFP4_EINVAL  # alignment
+    assert b"256-byte" in L.nvfp4_last_error()

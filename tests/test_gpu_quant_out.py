@@ -1,5 +1,6 @@
 """GPU parity of nvfp4_gemm_quant_out: the NVFP4 GEMM whose epilogue
-quantizes Y for the next layer (Eq. 3 / Eq. 2 with a static output scale).
+quantizes Y for the next layer (Eq. 3 / Eq. 2 with a static output scale),
+and of nvfp4_gemm_quant_out_dynamic (the output scale from Y's own amax).
 
 Where floating point decides the codes, both sides decide in the same
 precision: the oracle's FP32 quantizer is applied to the FP32 output of the
@@ -126,3 +127,94 @@ def test_quant_out_k_zero_and_errors(nv):
     rc = nv.lib().nvfp4_gemm_quant_out(nv._ptr(a), nv._ptr(s), nv._ptr(one), nv._ptr(w), nv._ptr(ws), nv._ptr(one),
                                        4, 24, 16, nv._ptr(yc2), nv._ptr(ys2), nv._ptr(one), nv._stream(None))
     assert rc == nv.NVFP4_EINVAL and "multiple of 16" in nv.last_error()
+
+
+def _check_dynamic(nv, oracle_mod, A, W, what, ref=None, pairs=None):
+    """Dynamic output scale: alpha_Y, codes and scales bit-exact against the
+    oracle's FP32 quantizer (dynamic alpha) on the tile GEMM's FP32 output."""
+    y32 = _tile_fp32(nv, A, W)
+    if ref is not None:
+        parity.assert_gemm_close(y32, ref, parity.GEMM_TOL_F32, what + " fp32")
+    if pairs is not None:
+        mi, ni, pref = pairs
+        parity.assert_gemm_close(y32[mi, ni], pref, parity.GEMM_TOL_F32, what + " fp32 sampled")
+    yc, ys, ya = nv.nvfp4_gemm_quant_out_dynamic(u8_dev(A[0]), u8_dev(A[1]), f32_dev([A[2]]), u8_dev(W[0]),
+                                                 u8_dev(W[1]), f32_dev([W[2]]))
+    want_c, want_s, want_a = oracle_mod.quantize_f32(y32)
+    assert host(ya)[0] == want_a, f"{what}: alpha {host(ya)[0]!r} != {want_a!r}"
+    got_c, got_s = host(yc), host(ys)
+    assert np.array_equal(got_s, want_s), f"{what}: {np.count_nonzero(got_s != want_s)} scale mismatches"
+    assert np.array_equal(got_c, want_c), f"{what}: {np.count_nonzero(got_c != want_c)} code mismatches"
+    return yc, ys, ya
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 256), (1, 16, 16), (33, 48, 96), (130, 272, 272), (300, 528, 1024),
+                                   (257, 1040, 4096), (512, 512, 512)])
+def test_quant_out_dynamic_shapes(nv, oracle_mod, M, N, K):
+    g = np.random.default_rng(M * 5 + N + K * 3)
+    A = oracle_mod.quantize(wl.activations(M, K, g))
+    W = oracle_mod.quantize(wl.weights(N, K, g))
+    say("gemm quant out dynamic", M, N, K)
+    _check_dynamic(nv, oracle_mod, A, W, f"dynamic {M}x{N}x{K}", ref=oracle_mod.gemm_exact(*A, *W))
+
+
+def test_quant_out_dynamic_matches_static_with_its_alpha(nv, oracle_mod):
+    """With the dynamic call's alpha_Y passed as a static scale, the epilogue
+    quantizer gives the same codes and scales."""
+    M, N, K = 300, 528, 1024
+    g = np.random.default_rng(23)
+    A = oracle_mod.quantize(wl.activations(M, K, g))
+    W = oracle_mod.quantize(wl.weights(N, K, g))
+    say("gemm quant out dynamic vs static")
+    yc, ys, ya = _check_dynamic(nv, oracle_mod, A, W, "dynamic vs static")
+    sc, ss = nv.nvfp4_gemm_quant_out(u8_dev(A[0]), u8_dev(A[1]), f32_dev([A[2]]), u8_dev(W[0]), u8_dev(W[1]),
+                                     f32_dev([W[2]]), ya)
+    assert np.array_equal(host(sc), host(yc)) and np.array_equal(host(ss), host(ys))
+
+
+def test_quant_out_dynamic_qwen3_8b_o_proj_full(nv, oracle_mod):
+    """The O projection of Qwen3-8B at 8192 tokens (8192 x 4096 x 4096), every
+    output code and scale and the output tensor scale."""
+    w = wl.WORKLOADS["qwen3_8b_m8192"]
+    name, K, N = w.linears[1]
+    a, wt = wl.layer_inputs(w, 1)
+    say("gemm quant out dynamic qwen3-8b", name, (w.M, N, K))
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    g = np.random.default_rng(6)
+    mi = np.concatenate([g.integers(0, w.M, 4096), [0, w.M - 1]])
+    ni = np.concatenate([g.integers(0, N, 4096), [N - 1, 0]])
+    pref = oracle_mod.gemm_exact_pairs(*A, *W, mi, ni)
+    _check_dynamic(nv, oracle_mod, A, W, "dynamic qwen3-8b o_proj", pairs=(mi, ni, pref))
+
+
+def test_quant_out_dynamic_two_calls_reuse_workspace(nv, oracle_mod):
+    """One workspace for two calls in a row (larger, then smaller product):
+    the second result does not depend on what the first left behind."""
+    import torch
+
+    say("gemm quant out dynamic workspace reuse")
+    big = (384, 512, 512)
+    ws = torch.empty(nv.gemm_quant_out_dynamic_workspace_size(*big), dtype=torch.uint8, device="cuda")
+    for i, (M, N, K) in enumerate((big, (65, 64, 256))):
+        g = np.random.default_rng(70 + i)
+        A = oracle_mod.quantize(wl.activations(M, K, g))
+        W = oracle_mod.quantize(wl.weights(N, K, g))
+        yc, ys, ya = nv.nvfp4_gemm_quant_out_dynamic(u8_dev(A[0]), u8_dev(A[1]), f32_dev([A[2]]), u8_dev(W[0]),
+                                                     u8_dev(W[1]), f32_dev([W[2]]), workspace=ws)
+        want_c, want_s, want_a = oracle_mod.quantize_f32(_tile_fp32(nv, A, W))
+        assert host(ya)[0] == want_a
+        assert np.array_equal(host(ys), want_s) and np.array_equal(host(yc), want_c)
+
+
+def test_quant_out_dynamic_k_zero(nv):
+    import torch
+
+    say("gemm quant out dynamic K=0")
+    z = torch.empty((4, 0), dtype=torch.uint8, device="cuda")
+    w0 = torch.empty((16, 0), dtype=torch.uint8, device="cuda")
+    one = f32_dev([1.0])
+    yc = torch.full((4, 8), 0x77, dtype=torch.uint8, device="cuda")
+    ys = torch.full((4, 1), 0x77, dtype=torch.uint8, device="cuda")
+    ya = f32_dev([3.0])
+    nv.nvfp4_gemm_quant_out_dynamic(z, z, one, w0, w0, one, yc, ys, ya)
+    assert not host(yc).any() and not host(ys).any() and host(ya)[0] == 0.0
