@@ -223,6 +223,21 @@ def main():
     quant_ms_total = sum(v["quant_us"] for v in per_layer.values()) / 1e3
     quant_bytes = sum(M * L["K"] * 4.5625 for L in layers)
 
+    # practical HBM yardstick for the quantizer: a plain 1 GiB device copy
+    # (reads 1 GiB, writes 1 GiB; larger than the 256 MB Infinity Cache)
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    cs_, ce_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cs_.record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    ce_.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (cs_.elapsed_time(ce_) * 1e-3) / 1e9
+    del csrc, cdst
+
     # dominant kernel: the gate_up NVFP4 GEMM launch
     gu = per_layer["gate_up"]
     gu_flops = wl.flops(M, gu["N"], gu["K"])
@@ -248,6 +263,8 @@ def main():
         "frac_f16_mfma_peak": round(value / F16_PEAK_TFLOPS, 4),
         "gemm_only_tflops": round(flops_step / (gemm_ms_total * 1e-3) / 1e12, 2),
         "quantizer_gbps": round(quant_bytes / (quant_ms_total * 1e-3) / 1e9, 1),
+        "hbm_copy_gbps": round(copy_gbps, 1),
+        "quantizer_frac_of_copy": round(quant_bytes / (quant_ms_total * 1e-3) / 1e9 / copy_gbps, 3),
         "per_layer": per_layer,
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
         "kernel_ms_per_step": round(kern_ms, 4),
