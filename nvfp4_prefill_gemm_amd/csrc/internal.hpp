@@ -94,6 +94,7 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int
 enum DecodeKind { DECODE_BF16 = 0, DECODE_NVFP4 = 1, DECODE_FUSED = 2 };
 struct DecodePlan {
     int ng, waves, u, s;  // 16-column groups per workgroup, waves, K steps per stage, K slices
+    bool pipe = true;     // K loop with each stage's loads pinned ahead of the other's MFMAs
 };
 DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K);
 // NVFP4 decode of one or two batch rows with K % 128 == 0 runs the weight

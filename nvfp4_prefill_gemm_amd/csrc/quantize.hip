@@ -119,7 +119,10 @@ enum AlphaSrc { ALPHA_STATIC = 0, ALPHA_PARTIALS = 1, ALPHA_SELF = 2 };
 // Max |x| over a whole small tensor (at most kSelfLoads * kThreads octets)
 // by one workgroup, as FP32 bits of the BF16 maximum: every workgroup of the
 // single-launch mode reads the tensor once, all its loads in flight together,
-// instead of waiting for a separate amax launch.
+// instead of waiting for a separate amax launch.  Slots past the tensor
+// load its first octet again (it is part of the tensor, so the maximum is
+// unchanged): the loads carry no condition and are all issued before the
+// first use, so they are in flight together.
 constexpr int kSelfLoads = 16;
 __device__ __forceinline__ uint32_t tensor_amax_bits(const uint16_t *__restrict__ x, uint32_t rows, uint32_t octs,
                                                      int64_t ld) {
@@ -127,10 +130,10 @@ __device__ __forceinline__ uint32_t tensor_amax_bits(const uint16_t *__restrict_
     uint4 v[kSelfLoads];
 #pragma unroll
     for (int u = 0; u < kSelfLoads; ++u) {
-        const uint32_t o = threadIdx.x + u * kThreads, r = o < total ? o / octs : 0u;
-        v[u] = o < total ? *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (o - r * octs) * 8)
-                         : make_uint4(0, 0, 0, 0);
+        const uint32_t o = threadIdx.x + u * kThreads, oc = o < total ? o : 0u, r = oc / octs;
+        v[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (oc - r * octs) * 8);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
     ushort2_t m = {0, 0};
 #pragma unroll
     for (int u = 0; u < kSelfLoads; ++u) {

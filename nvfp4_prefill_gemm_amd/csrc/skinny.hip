@@ -106,11 +106,11 @@ __device__ __forceinline__ void slice_steps(int64_t steps, int64_t sps, int64_t 
     se = sb + sps < steps ? sb + sps : steps;
 }
 
-template <int MG, int NG, int WAVES, int U, int kOut>
+template <int MG, int NG, int WAVES, int U, int kOut, bool kPipe>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                             int64_t M, int64_t N, int64_t K, void *__restrict__ out,
                                                             int64_t ld_out, int64_t sps) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int kq = (lane >> 4) * 8;
     int64_t sb, se;
@@ -163,18 +163,39 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
     const int64_t stride = (int64_t)WAVES * U;
     WStage bw0, bw1;
     XStage ax0, ax1;
-    int64_t ks0 = sb + wave;
-    load(ks0, bw0, ax0);
-    for (;;) {
-        const int64_t k1 = ks0 + stride;
-        load(k1, bw1, ax1);
-        compute(bw0, ax0);
-        if (k1 >= se) break;
-        const int64_t k2 = k1 + stride;
-        load(k2, bw0, ax0);
-        compute(bw1, ax1);
-        if (k2 >= se) break;
-        ks0 = k2;
+    int64_t k = sb + wave;
+    load(k, bw0, ax0);
+    if constexpr (kPipe) {
+        // Two steps per trip with no exit test between a stage's loads and
+        // its MFMAs: given one, the compiler sinks the loads past it to their
+        // use and then waits for every load before each step.  The
+        // scheduling barriers keep each stage's loads ahead of the other
+        // stage's MFMAs, so one stage is always in flight.  A step past the
+        // slice reads zeros (at most one per wave; its MFMAs add nothing).
+        for (;;) {
+            load(k + stride, bw1, ax1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(bw0, ax0);
+            load(k + 2 * stride, bw0, ax0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(bw1, ax1);
+            k += 2 * stride;
+            if (k >= se) break;
+        }
+    } else {
+        // the compiler's own schedule: both stages' loads issued together,
+        // then both consumed (faster for one column group of 16 waves)
+        for (;;) {
+            const int64_t k1 = k + stride;
+            load(k1, bw1, ax1);
+            compute(bw0, ax0);
+            if (k1 >= se) break;
+            const int64_t k2 = k1 + stride;
+            load(k2, bw0, ax0);
+            compute(bw1, ax1);
+            if (k2 >= se) break;
+            k = k2;
+        }
     }
 
     tile_reduce<MG, NG, WAVES, kOut>(acc, 1.0f, 1.0f, M, N, n0, out, ld_out);
@@ -199,7 +220,7 @@ enum ASrc { A_NVFP4 = 0, A_BF16_DYNAMIC = 1, A_BF16_STATIC = 2 };
 // A lane holds rows 4 (l / 16) + i, i.e. batch row l / 32 and blocks
 // 4 ((l / 16) % 2) + i of every chunk; the four block sums of a lane and the
 // two lanes of a batch row are added at the end.
-template <int MG, int NG, int WAVES, int U, int kOut, int kA = A_NVFP4, bool kF4 = false>
+template <int MG, int NG, int WAVES, int U, int kOut, int kA = A_NVFP4, bool kF4 = false, bool kPipe = true>
 __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, float *__restrict__ a_alpha,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, const float *__restrict__ w_alpha, int64_t M,
@@ -207,7 +228,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     int64_t sps) {
     static_assert(kA == A_NVFP4 || MG == 1, "BF16 activations: one 16-row group");
     static_assert(!kF4 || MG == 1, "the FP4-MFMA path takes at most two batch rows");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int64_t cb = K >> 1, sb = K >> 4;  // code and scale bytes per row
     int64_t cs, ce;                          // this slice's 128-wide K chunks [cs, ce)
@@ -480,16 +501,29 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     int64_t c0 = cs + wave;
     if constexpr (kA != A_NVFP4) load_part(c0, s0, false, true);  // the weights are in flight already
     else load(c0, s0);
-    for (;;) {
-        const int64_t c1 = c0 + stride;
-        load(c1, s1);
-        compute(s0);
-        if (c1 >= ce) break;
-        const int64_t c2 = c1 + stride;
-        load(c2, s0);
-        compute(s1);
-        if (c2 >= ce) break;
-        c0 = c2;
+    if constexpr (kPipe) {  // two chunk stages per trip, as in the BF16 decode kernel
+        for (;;) {
+            load(c0 + stride, s1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(s0);
+            load(c0 + 2 * stride, s0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(s1);
+            c0 += 2 * stride;
+            if (c0 >= ce) break;
+        }
+    } else {  // the compiler's own schedule (faster for 4 x 4 tiles split over K)
+        for (;;) {
+            const int64_t c1 = c0 + stride;
+            load(c1, s1);
+            compute(s0);
+            if (c1 >= ce) break;
+            const int64_t c2 = c1 + stride;
+            load(c2, s0);
+            compute(s1);
+            if (c2 >= ce) break;
+            c0 = c2;
+        }
     }
 
     if constexpr (kF4) {
@@ -552,8 +586,9 @@ hipError_t launch_reduce(const float *part, int S, int64_t M, int64_t N, const f
 int64_t steps_per_slice(int64_t steps, int S) { return S <= 1 ? (steps > 0 ? steps : 1) : (steps + S - 1) / S; }
 
 // BF16 decode kernel with NG column groups, WAVES waves, U steps per stage,
-// S slices of K (S > 1: partials into `part`, then the reduction kernel).
-template <int MG, int NG, int WAVES, int U>
+// S slices of K (S > 1: partials into `part`, then the reduction kernel);
+// kPipe: the pinned two-stage loop, else the compiler's schedule.
+template <int MG, int NG, int WAVES, int U, bool kPipe = true>
 hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
                            int out_type, int64_t ld_out, int S, float *part, hipStream_t s) {
     const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
@@ -562,23 +597,23 @@ hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int6
     const int ns = S > 1 ? (int)((((K + 31) >> 5) + sps - 1) / sps) : 1;
     const dim3 grid((unsigned)nb, (unsigned)ns), block(WAVES * 64);
     if (ns > 1) {
-        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_PARTIAL>), grid, block, 0, s, a, w, M, N, K,
+        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kPipe>), grid, block, 0, s, a, w, M, N, K,
                            (void *)part, N, sps);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         return launch_reduce(part, ns, M, N, nullptr, nullptr, out, out_type, ld_out, s);
     }
     if (out_type == OUT_BF16)
-        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_BF16>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
+        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_BF16, kPipe>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
                            sps);
     else
-        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_F32>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
+        hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_F32, kPipe>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
                            sps);
     return hipGetLastError();
 }
 
 // NVFP4 decode kernel (kA: NVFP4 activations, or BF16 ones quantized inside;
-// kF4: the FP4-MFMA form, for M <= 2 and K % 128 == 0).
-template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4, bool kF4 = false>
+// kF4: the FP4-MFMA form, for M <= 2 and K % 128 == 0; kPipe as above).
+template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4, bool kF4 = false, bool kPipe = true>
 hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
                             const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
                             int S, float *part, hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0) {
@@ -588,9 +623,9 @@ hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, con
     const int ns = S > 1 ? (int)((chunks + sps - 1) / sps) : 1;
     const size_t lds = kA == A_NVFP4 ? 0 : (size_t)(M * K / 2 + M * K / 16);
     const int kind = ns > 1 ? DOUT_PARTIAL : out_type == OUT_BF16 ? DOUT_BF16 : DOUT_F32;
-    const void *f = kind == DOUT_PARTIAL ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4>
-                    : kind == DOUT_BF16  ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4>
-                                         : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4>;
+    const void *f = kind == DOUT_PARTIAL ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4, kPipe>
+                    : kind == DOUT_BF16  ? (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4, kPipe>
+                                         : (const void *)skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4, kPipe>;
     if (kA != A_NVFP4) {
         static std::atomic<uint32_t> attr_done[3];
         if (hipError_t e = set_dyn_lds_once(attr_done[kind], f, (int)(kFusedDecodeMaxElems * 9 / 16)); e != hipSuccess)
@@ -600,13 +635,13 @@ hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, con
     void *dst = ns > 1 ? (void *)part : out;
     const int64_t ld = ns > 1 ? N : ld_out;
     if (kind == DOUT_PARTIAL)
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4>), grid, block, lds, s, ac, as, aa,
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4, kPipe>), grid, block, lds, s, ac, as, aa,
                            wc, ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     else if (kind == DOUT_BF16)
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4>), grid, block, lds, s, ac, as, aa, wc,
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4, kPipe>), grid, block, lds, s, ac, as, aa, wc,
                            ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     else
-        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4>), grid, block, lds, s, ac, as, aa, wc,
+        hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4, kPipe>), grid, block, lds, s, ac, as, aa, wc,
                            ws, wa, M, N, K, dst, ld, x, ld_x, sps);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if (ns > 1) return launch_reduce(part, ns, M, N, aa, wa, out, out_type, ld_out, s);
@@ -635,9 +670,13 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
         if (K >= 8192) return {1, 16, 1, 1};
         return {1, 8, 2, 1};
     }
+    // pipe = false (the compiler's schedule of the K loop) where it measured
+    // faster: one column group of 16 waves (BF16: batch 1 qkv / o / down
+    // 13.6 / 8.2 / 21.4 us against 13.9 / 8.9 / 23.8 with the pinned loop)
+    // and 4 x 4 NVFP4 tiles split over K (down at batch 64: 24.8 against 26.9)
     if (kind == DECODE_BF16) {
-        if (M <= 4) return {1, 16, 1, 1};
-        if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1};
+        if (M <= 4) return {1, 16, 1, 1, false};
+        if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1, false};
         // wide layers at batch 33-64: 128-column strips read the batch once
         // per 128 columns instead of per 64 (gate_up at batch 64: 77.9 -> 69.8 us)
         if (M > 32 && N >= 16384) return {8, 4, 1, 1};
@@ -648,8 +687,10 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
     }
     // NVFP4 and fused: the same plan, so both sum in the same order
     if (M <= 16) return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 16, 1, 1};
-    if (K >= 8192) return {4, 8, 1, 4};
-    if (N >= 16384 && M > 32) return {4, 8, 1, 1};
+    if (K >= 8192) return {4, 8, 1, 4, false};
+    // wide layers at batch 33-64: 32-column strips of 4 waves, two chunks per
+    // stage (gate_up at batch 64: 42.9 us against 47.2 with 64-column strips)
+    if (N >= 16384 && M > 32) return {2, 4, 2, 1};
     return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 8, 2, 1};
 }
 
@@ -673,6 +714,8 @@ hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64
     if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 2) return launch_bf16_cfg<MG, 2, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
+    if constexpr (MG == 1)
+        if (!p.pipe) return launch_bf16_cfg<1, 1, 16, 1, false>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
     return launch_bf16_cfg<MG, 1, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
 }
 
@@ -699,7 +742,13 @@ hipError_t launch_nv_mg(const uint8_t *ac, const uint8_t *as, const float *aa_in
     if constexpr (MG == 1)
         if (decode_fp4_form(M, K))
             return launch_f4<A_NVFP4>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, nullptr, 0);
+    if (p.ng == 4 && !p.pipe)
+        return launch_nvfp4_cfg<MG, 4, 8, 1, A_NVFP4, false, false>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type,
+                                                                    ld_out, S, part, s);
     if (p.ng == 4) return launch_nvfp4_cfg<MG, 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+    if constexpr (MG == 4)
+        if (p.ng == 2 && p.waves == 4)
+            return launch_nvfp4_cfg<4, 2, 4, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.ng == 2) return launch_nvfp4_cfg<MG, 2, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
     if (p.waves == 8)
         return launch_nvfp4_cfg<MG, 1, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
