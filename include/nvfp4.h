@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 enum {
     NVFP4_OK = 0,
@@ -214,6 +214,56 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
                      const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                      int64_t M, int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode-packed NVFP4 weights for the decode kernels (the uniform-NVFP4
+ * decode variant of Mix-Quant Section 4; decode is bound by moving the
+ * weights, Section 3.1).  The row-major layout above makes a decode wave's
+ * 16-byte loads gather 16 rows per instruction and its block-scale loads
+ * scatter; the packed layout stores, for every group of 16 weight rows g and
+ * every 128-wide K chunk c, one 1152-byte block at offset
+ * (g * K / 128 + c) * 1152:
+ *   bytes [0, 1024): byte 16 l + b = code byte 64 c + 16 (l / 16) + b of row
+ *                    16 g + l % 16 (l = 0..63, b = 0..15)
+ *   bytes [1024, 1152): byte 8 r + t = scale byte 8 c + t of row 16 g + r
+ * Rows past N are zeros.  Same codes and scales, so the packed entry points
+ * below give the row-major ones' results bit for bit.
+ *   nvfp4_decode_pack_size: bytes of the packed weight (0 if N <= 0, K <= 0
+ *   or K % 128 != 0).
+ *   nvfp4_decode_pack: w_codes [N, K/2] (16-byte aligned), w_scales
+ *   [N, K/16] (4-byte aligned) -> w_packed (16-byte aligned, caller-owned,
+ *   nvfp4_decode_pack_size bytes).  K % 128 != 0: NVFP4_EUNSUPPORTED.
+ */
+size_t nvfp4_decode_pack_size(int64_t N, int64_t K);
+int nvfp4_decode_pack(const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, int64_t K,
+                      uint8_t *w_packed, void *stream);
+
+/*
+ * nvfp4_gemm on decode-packed weights: decode batches only (M <= 64; K % 128
+ * == 0 and K < 2^24, else NVFP4_EUNSUPPORTED).  Operands other than the
+ * weight, out and workspace (nvfp4_gemm_workspace_size(M, N, K) bytes for
+ * the split-K partials) as in nvfp4_gemm; results equal nvfp4_gemm's on the
+ * row-major weight bit for bit.
+ */
+int nvfp4_gemm_packed(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                      const uint8_t *w_packed, const float *w_alpha, int64_t M, int64_t N, int64_t K,
+                      void *out, int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * nvfp4_quant_gemm on decode-packed weights (M <= 64, K % 128 == 0, K < 2^24,
+ * else NVFP4_EUNSUPPORTED): the fused decode kernel for the batches
+ * nvfp4_quant_gemm routes to it, otherwise the quantizer into the workspace
+ * and the decode kernel.  workspace: nvfp4_quant_gemm_workspace_size(M, N, K)
+ * bytes; the fused batches need only what nvfp4_quant_gemm needs for them,
+ * the others at least the quantized batch (codes, scales, amax partials),
+ * else NVFP4_EWORKSPACE.  Results equal nvfp4_quant_gemm's on the row-major
+ * weight bit for bit.
+ */
+int nvfp4_quant_gemm_packed(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha_mode,
+                            const uint8_t *w_packed, const float *w_alpha, int64_t M, int64_t N, int64_t K,
+                            void *out, int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Bytes of device workspace bf16_gemm uses at these sizes for its fastest
  * kernels (0: none); as nvfp4_gemm_workspace_size. */

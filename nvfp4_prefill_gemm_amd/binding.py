@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from typing import NamedTuple
 
 import torch
 
@@ -35,6 +36,10 @@ _SIGNATURES = {
     "nvfp4_gemm_quant_out_dynamic": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_quant_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quant_gemm": (_I, [_P, _I64, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
+    "nvfp4_decode_pack_size": (_SZ, [_I64, _I64]),
+    "nvfp4_decode_pack": (_I, [_P, _P, _I64, _I64, _P, _P]),
+    "nvfp4_gemm_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
+    "nvfp4_quant_gemm_packed": (_I, [_P, _I64, _P, _I, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "bf16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "bf16_gemm": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "mxfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
@@ -377,6 +382,108 @@ def nvfp4_quant_gemm(x: torch.Tensor, w_codes, w_scales, w_alpha, a_alpha: torch
                                 _ptr(w_scales), _ptr(w_alpha), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0),
                                 _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check("nvfp4_quant_gemm", rc)
+    return out, a_alpha
+
+
+class DecodePackedWeight(NamedTuple):
+    """An NVFP4 weight [N, K] in the decode-packed layout (include/nvfp4.h):
+    ``packed`` uint8 [decode_pack_size(N, K)], ``alpha`` float32 [1]."""
+    packed: torch.Tensor
+    alpha: torch.Tensor
+    n: int
+    k: int
+
+
+def decode_pack_size(N: int, K: int) -> int:
+    return int(lib().nvfp4_decode_pack_size(N, K))
+
+
+def _packed_weight(wp, K: int | None = None):
+    if not isinstance(wp, DecodePackedWeight):
+        raise TypeError(f"the weight must be a DecodePackedWeight, got {type(wp).__name__}")
+    if K is not None and wp.k != K:
+        raise ValueError(f"activations and the packed weight disagree on K ({K} vs {wp.k})")
+    if wp.k % 128:
+        raise ValueError(f"packed weight: K = {wp.k} must be a multiple of 128")
+    _tensor(wp.packed, "packed")
+    if wp.packed.dtype != torch.uint8 or wp.packed.dim() != 1 or not wp.packed.is_contiguous():
+        raise ValueError("packed must be a contiguous 1-D uint8 tensor")
+    if wp.packed.numel() != decode_pack_size(wp.n, wp.k):
+        raise ValueError(f"packed holds {wp.packed.numel()} bytes, the layout of [{wp.n}, {wp.k}] takes "
+                         f"{decode_pack_size(wp.n, wp.k)}")
+    _alpha(wp.alpha, "w_alpha")
+    return wp
+
+
+def nvfp4_decode_pack(w_codes, w_scales, w_alpha, packed: torch.Tensor | None = None,
+                      stream=None) -> DecodePackedWeight:
+    """Row-major NVFP4 weight (codes [N, K/2], scales [N, K/16], alpha [1]) ->
+    the decode-packed layout the *_packed GEMMs stream (K % 128 == 0)."""
+    _mat(w_codes, "w_codes", torch.uint8)
+    K = _k_of_codes(w_codes, "w_codes", 128)
+    N = w_codes.shape[0]
+    _mat(w_scales, "w_scales", torch.uint8, N, K // 16)
+    _alpha(w_alpha, "w_alpha")
+    if packed is None:
+        packed = torch.empty(decode_pack_size(N, K), dtype=torch.uint8, device=w_codes.device)
+    wp = _packed_weight(DecodePackedWeight(packed, w_alpha, N, K))
+    _same_device(("w_codes", w_codes), ("w_scales", w_scales), ("w_alpha", w_alpha), ("packed", packed))
+    rc = lib().nvfp4_decode_pack(_ptr(w_codes), _ptr(w_scales), N, K, _ptr(packed), _stream(stream))
+    _check("nvfp4_decode_pack", rc)
+    return wp
+
+
+def nvfp4_gemm_packed(a_codes, a_scales, a_alpha, wp: DecodePackedWeight, out: torch.Tensor | None = None,
+                      out_dtype=torch.bfloat16, workspace=None, stream=None) -> torch.Tensor:
+    """nvfp4_gemm on a decode-packed weight (M <= 64)."""
+    _mat(a_codes, "a_codes", torch.uint8)
+    K = _k_of_codes(a_codes, "a_codes")
+    M = a_codes.shape[0]
+    _mat(a_scales, "a_scales", torch.uint8, M, K // 16)
+    _alpha(a_alpha, "a_alpha")
+    _packed_weight(wp, K)
+    N = wp.n
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _out(out, "out", M, N)
+    _same_device(("a_codes", a_codes), ("a_scales", a_scales), ("a_alpha", a_alpha), ("packed", wp.packed),
+                 ("w_alpha", wp.alpha), ("out", out),
+                 ("workspace", workspace if isinstance(workspace, torch.Tensor) else None))
+    workspace = _workspace(workspace, gemm_workspace_size(M, N, K) if workspace is None else 0, a_codes.device)
+    rc = lib().nvfp4_gemm_packed(_ptr(a_codes), _ptr(a_scales), _ptr(a_alpha), _ptr(wp.packed), _ptr(wp.alpha),
+                                 M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0), _ptr(workspace),
+                                 _nbytes(workspace), _stream(stream))
+    _check("nvfp4_gemm_packed", rc)
+    return out
+
+
+def nvfp4_quant_gemm_packed(x: torch.Tensor, wp: DecodePackedWeight, a_alpha: torch.Tensor | None = None,
+                            static_alpha: bool = False, out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                            workspace: torch.Tensor | None = None, stream=None):
+    """nvfp4_quant_gemm on a decode-packed weight (M <= 64).  Returns (out, a_alpha)."""
+    _mat(x, "x", torch.bfloat16, contiguous=False)
+    M, K = x.shape
+    _packed_weight(wp, K)
+    N = wp.n
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _out(out, "out", M, N)
+    if a_alpha is None:
+        if static_alpha:
+            raise ValueError("static_alpha needs a_alpha")
+        a_alpha = torch.empty(1, dtype=torch.float32, device=x.device)
+    _alpha(a_alpha, "a_alpha")
+    if workspace is not None:
+        _tensor(workspace, "workspace")
+    _same_device(("x", x), ("packed", wp.packed), ("w_alpha", wp.alpha), ("out", out), ("a_alpha", a_alpha),
+                 ("workspace", workspace))
+    if workspace is None:
+        workspace = torch.empty(max(quant_gemm_workspace_size(M, N, K), 16), dtype=torch.uint8, device=x.device)
+    rc = lib().nvfp4_quant_gemm_packed(_ptr(x), x.stride(0), _ptr(a_alpha),
+                                       NVFP4_ALPHA_STATIC if static_alpha else NVFP4_ALPHA_DYNAMIC,
+                                       _ptr(wp.packed), _ptr(wp.alpha), M, N, K, _ptr(out), _OUT[out.dtype],
+                                       out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("nvfp4_quant_gemm_packed", rc)
     return out, a_alpha
 
 

@@ -388,4 +388,114 @@ int mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w
                       "mx gemm kernel");
 }
 
+size_t nvfp4_decode_pack_size(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % 128 != 0) return 0;
+    return (size_t)((N + 15) / 16) * (size_t)(K / 128) * (size_t)nvfp4::kPackBlock;
+}
+
+int nvfp4_decode_pack(const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, int64_t K, uint8_t *w_packed,
+                      void *stream) {
+    const char *fn = "nvfp4_decode_pack";
+    if (N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (K % 128 != 0) return fail(NVFP4_EUNSUPPORTED, "%s: K (%lld) must be a multiple of 128", fn, (long long)K);
+    if (N == 0 || K == 0) return ok();
+    if (!w_codes || !w_scales || !w_packed) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
+    if (!aligned(w_codes, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 4))
+        return fail(NVFP4_EINVAL, "%s: codes and w_packed must be 16-byte, scales 4-byte aligned", fn);
+    return hip_status(nvfp4::launch_decode_pack(w_codes, w_scales, N, K, w_packed, as_stream(stream)), "pack kernel");
+}
+
+namespace {
+
+// shapes the decode-packed entry points take: 0 <= M <= 64, N >= 0,
+// K % 128 == 0, K < 2^24
+int check_packed_shape(int64_t M, int64_t N, int64_t K, const char *fn) {
+    if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (M > nvfp4::kSkinnyMaxM)
+        return fail(NVFP4_EUNSUPPORTED, "%s: M (%lld) above %lld (decode batches only)", fn, (long long)M,
+                    (long long)nvfp4::kSkinnyMaxM);
+    if (K % 128 != 0 || K >= nvfp4::kSkinnyMaxK)
+        return fail(NVFP4_EUNSUPPORTED, "%s: K (%lld) must be a multiple of 128 below 2^24", fn, (long long)K);
+    return NVFP4_OK;
+}
+
+int check_packed_w(const uint8_t *w_packed, const float *w_alpha, const char *fn) {
+    if (!w_packed || !w_alpha) return fail(NVFP4_EINVAL, "%s: w_packed and w_alpha must be non-null", fn);
+    if (!aligned(w_packed, 16)) return fail(NVFP4_EINVAL, "%s: w_packed must be 16-byte aligned", fn);
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+int nvfp4_gemm_packed(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha, const uint8_t *w_packed,
+                      const float *w_alpha, int64_t M, int64_t N, int64_t K, void *out, int out_dtype, int64_t ld_out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "nvfp4_gemm_packed";
+    int rc = check_packed_shape(M, N, K, fn);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return ok();
+    if ((rc = check_out(out, out_dtype, N, ld_out, fn))) return rc;
+    hipStream_t s = as_stream(stream);
+    const int esz = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
+    if ((rc = check_packed_w(w_packed, w_alpha, fn))) return rc;
+    if ((rc = check_nvfp4(a_codes, a_scales, a_alpha, "A", fn))) return rc;
+    if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    return hip_status(nvfp4::launch_skinny_nvfp4(a_codes, a_scales, a_alpha, w_packed, nullptr, w_alpha, M, N, K, out,
+                                                 out_dtype, ld_out, workspace, workspace_bytes, s, true),
+                      "nvfp4 decode kernel");
+}
+
+int nvfp4_quant_gemm_packed(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha_mode,
+                            const uint8_t *w_packed, const float *w_alpha, int64_t M, int64_t N, int64_t K, void *out,
+                            int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "nvfp4_quant_gemm_packed";
+    int rc = check_packed_shape(M, N, K, fn);
+    if (rc) return rc;
+    if (alpha_mode != NVFP4_ALPHA_DYNAMIC && alpha_mode != NVFP4_ALPHA_STATIC)
+        return fail(NVFP4_EINVAL, "%s: bad alpha_mode %d", fn, alpha_mode);
+    if (M == 0 || N == 0) return ok();
+    if ((rc = check_out(out, out_dtype, N, ld_out, fn))) return rc;
+    hipStream_t s = as_stream(stream);
+    const int esz = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
+    if ((rc = check_packed_w(w_packed, w_alpha, fn))) return rc;
+    if (!x_bf16 || !a_alpha) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
+    if (ld_x < K || ld_x % 8 != 0) return fail(NVFP4_EINVAL, "%s: ld_x must be >= K and a multiple of 8", fn);
+    if (!aligned(x_bf16, 16)) return fail(NVFP4_EINVAL, "%s: x must be 16-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    const bool dyn = alpha_mode == NVFP4_ALPHA_DYNAMIC;
+    if (fused_decode_shape(M, N, K)) {
+        if (dyn) {
+            const size_t need = (size_t)nvfp4::amax_parts(M, K) * sizeof(uint32_t);
+            if (!workspace || workspace_bytes < need)
+                return fail(NVFP4_EWORKSPACE, "%s: dynamic alpha needs %zu workspace bytes", fn, need);
+        }
+        return hip_status(nvfp4::launch_skinny_fused((const uint16_t *)x_bf16, ld_x, a_alpha, dyn, w_packed, nullptr,
+                                                     w_alpha, M, N, K, out, out_dtype, ld_out, workspace,
+                                                     workspace_bytes, s, true),
+                          "fused decode kernel");
+    }
+    // quantize the batch into the workspace, then the decode kernel
+    const QgLayout l = qg_layout(M, N, K, dyn);
+    if (!workspace || workspace_bytes < l.split)
+        return fail(NVFP4_EWORKSPACE, "%s: needs at least %zu workspace bytes (%zu with the split-K partials)", fn,
+                    l.split, l.total);
+    uint8_t *wsb = (uint8_t *)workspace;
+    uint8_t *codes = wsb + l.codes, *scales = wsb + l.scales;
+    const int nparts = nvfp4::amax_parts(M, K);
+    if (dyn && !nvfp4::quantize_self_amax(M, K) &&
+        (rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, M, K, ld_x,
+                                                     (uint32_t *)(wsb + l.parts), nparts, s),
+                         "amax kernel")))
+        return rc;
+    if ((rc = hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha, dyn,
+                                                (const uint32_t *)(wsb + l.parts), nparts, s),
+                         "quantize kernel")))
+        return rc;
+    return hip_status(nvfp4::launch_skinny_nvfp4(codes, scales, a_alpha, w_packed, nullptr, w_alpha, M, N, K, out,
+                                                 out_dtype, ld_out, wsb + l.split, workspace_bytes - l.split, s, true),
+                      "nvfp4 decode kernel");
+}
+
 }  // extern "C"

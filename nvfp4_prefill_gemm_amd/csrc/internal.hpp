@@ -108,21 +108,32 @@ size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
                               int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s);
 
+// Decode-packed NVFP4 weights (nvfp4_decode_pack): for every group of 16
+// rows g and 128-wide K chunk c, one block of kPackBlock bytes at
+// (g * K / 128 + c) * kPackBlock: 1024 code bytes, byte 16 l + b = code byte
+// 64 c + 16 (l / 16) + b of row 16 g + l % 16 (the 16 bytes lane l of a
+// decode wave loads), then 128 scale bytes, byte 8 r + t = scale 8 c + t of
+// row 16 g + r.  Rows past N are zeros.  Needs K % 128 == 0.
+constexpr int64_t kPackBlock = 1152;
+hipError_t launch_decode_pack(const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, int64_t K,
+                              uint8_t *w_packed, hipStream_t s);
+
 // NVFP4 x NVFP4 at decode shapes: M <= kSkinnyMaxM, K % 32 == 0, codes
 // 16-byte and scales 2-byte aligned (nvfp4_gemm checks and otherwise uses the
-// tile kernel).
+// tile kernel).  packed: w_codes is the decode-packed weight (w_scales
+// unused, K % 128 == 0).
 hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                                int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
-                               size_t ws_bytes, hipStream_t s);
+                               size_t ws_bytes, hipStream_t s, bool packed = false);
 
 // Fused decode (BF16 activations quantized into LDS by every workgroup):
 // M <= 16, M * K <= kFusedDecodeMaxElems, K % 32 == 0, x rows 16-byte
-// aligned; dynamic != 0 computes alpha_A in every workgroup.
+// aligned; dynamic != 0 computes alpha_A in every workgroup; packed as above.
 hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, int dynamic,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                                int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
-                               size_t ws_bytes, hipStream_t s);
+                               size_t ws_bytes, hipStream_t s, bool packed = false);
 
 // nvfp4_quant_gemm routes to the fused decode kernel batches of at most
 // kFusedDecodeMaxM rows with M * K <= kFusedDecodeMaxElems (108 KB of codes

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, float *__restrict__ a_alpha,
     const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, const float *__restrict__ w_alpha, int64_t M,
     int64_t N, int64_t K, void *__restrict__ out, int64_t ld_out, const uint16_t *__restrict__ x, int64_t ld_x,
-    int64_t sps) {
+    int64_t sps, int packed) {
     static_assert(kA == A_NVFP4 || MG == 1, "BF16 activations: one 16-row group");
     static_assert(!kF4 || MG == 1, "the FP4-MFMA path takes at most two batch rows");
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -242,17 +242,27 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
     // buffer resources over this workgroup's weight rows (and over A in global
-    // memory): rows past N or M and chunks past the slice or K read zeros
+    // memory): rows past N or M and chunks past the slice or K read zeros.
+    // Weight offsets are this lane's bytes of chunk 0 plus chunk * wstep:
+    // row-major codes [N, K/2] and scales [N, K/16] (steps 64 and 8), or the
+    // decode-packed blocks (one 1152-byte block per 16 rows and chunk, both
+    // steps 1152; rows past N are zeros in the last group's blocks).
     const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
-    const rsrc_t wcs = make_rsrc(wc + n0 * cb, (uint32_t)(nrows * cb));
-    const rsrc_t wss = make_rsrc(ws + n0 * sb, (uint32_t)(nrows * sb));
+    const int64_t nchunks = K >> 7, gbytes = nchunks * kPackBlock;  // packed bytes per 16-row group
+    const int64_t ngroups = (nrows + 15) >> 4;
+    const rsrc_t wcs = packed ? make_rsrc(wc + (n0 >> 4) * gbytes, (uint32_t)(ngroups * gbytes))
+                              : make_rsrc(wc + n0 * cb, (uint32_t)(nrows * cb));
+    const rsrc_t wss = packed ? wcs : make_rsrc(ws + n0 * sb, (uint32_t)(nrows * sb));
+    const uint32_t cstep = packed ? (uint32_t)kPackBlock : 64u, sstep = packed ? (uint32_t)kPackBlock : 8u;
     const rsrc_t xcs = make_rsrc(ac, (uint32_t)(M * cb));
     const rsrc_t xss = make_rsrc(as, (uint32_t)(M * sb));
     uint32_t wco[NG], wso[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-        wco[j] = (uint32_t)((j * 16 + (lane & 15)) * cb);
-        wso[j] = (uint32_t)((j * 16 + (lane & 15)) * sb);
+        const int r = j * 16 + (lane & 15);
+        wco[j] = packed ? (uint32_t)(j * gbytes + lane * 16) : (uint32_t)(r * cb + (lane >> 4) * 16);
+        wso[j] = packed ? (uint32_t)(j * gbytes + 1024 + (lane & 15) * 8 + (lane >> 4) * 2)
+                        : (uint32_t)(r * sb + (lane >> 4) * 2);
     }
     uint32_t xco[MG], xso[MG];
     bool xv[MG];
@@ -274,7 +284,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     const uint32_t f_so = (uint32_t)((f_sact ? (lane >> 5) : 0) * sb + 4 * (fg & 1));  // + 8 per chunk
     uint32_t f_wso[NG];
 #pragma unroll
-    for (int j = 0; j < NG; ++j) f_wso[j] = (uint32_t)((j * 16 + (lane & 15)) * sb + 4 * (fg & 1));
+    for (int j = 0; j < NG; ++j)
+        f_wso[j] = packed ? (uint32_t)(j * gbytes + 1024 + (lane & 15) * 8 + 4 * (fg & 1))
+                          : (uint32_t)((j * 16 + (lane & 15)) * sb + 4 * (fg & 1));
     const uint8_t *lc = nullptr, *ls = nullptr;  // LDS copy of A (fused path)
     float alpha_a = 0.0f;
     // Two register stages of U chunks each, as in the BF16 decode kernel.
@@ -296,8 +308,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
                 if (do_w) {
 #pragma unroll
                     for (int j = 0; j < NG; ++j) {
-                        st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + kc : kBufOOB);
-                        st.fws[u][j] = buf_load4(wss, kin ? f_wso[j] + (uint32_t)c * 8u : kBufOOB);
+                        st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + (uint32_t)c * cstep : kBufOOB);
+                        st.fws[u][j] = buf_load4(wss, kin ? f_wso[j] + (uint32_t)c * sstep : kBufOOB);
                     }
                 }
                 if (!do_x) continue;
@@ -316,8 +328,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
             if (do_w) {
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
-                    st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + kc : kBufOOB);
-                    st.wsc[u][j] = buf_load2(wss, kin ? wso[j] + ksc : kBufOOB);
+                    st.wq[u][j] = buf_load16(wcs, kin ? wco[j] + (uint32_t)c * cstep : kBufOOB);
+                    st.wsc[u][j] = buf_load2(wss, kin ? wso[j] + (uint32_t)c * sstep : kBufOOB);
                 }
             }
             if (!do_x) continue;
@@ -616,7 +628,8 @@ hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int6
 template <int MG, int NG, int WAVES, int U, int kA = A_NVFP4, bool kF4 = false, bool kPipe = true>
 hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
                             const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                            int S, float *part, hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0) {
+                            int S, float *part, hipStream_t s, const uint16_t *x = nullptr, int64_t ld_x = 0,
+                            int packed = 0) {
     const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t chunks = (K + 127) >> 7, sps = steps_per_slice(chunks, S);
@@ -636,16 +649,42 @@ hipError_t launch_nvfp4_cfg(const uint8_t *ac, const uint8_t *as, float *aa, con
     const int64_t ld = ns > 1 ? N : ld_out;
     if (kind == DOUT_PARTIAL)
         hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kA, kF4, kPipe>), grid, block, lds, s, ac, as, aa,
-                           wc, ws, wa, M, N, K, dst, ld, x, ld_x, sps);
+                           wc, ws, wa, M, N, K, dst, ld, x, ld_x, sps, packed);
     else if (kind == DOUT_BF16)
         hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_BF16, kA, kF4, kPipe>), grid, block, lds, s, ac, as, aa, wc,
-                           ws, wa, M, N, K, dst, ld, x, ld_x, sps);
+                           ws, wa, M, N, K, dst, ld, x, ld_x, sps, packed);
     else
         hipLaunchKernelGGL((skinny_nvfp4_kernel<MG, NG, WAVES, U, DOUT_F32, kA, kF4, kPipe>), grid, block, lds, s, ac, as, aa, wc,
-                           ws, wa, M, N, K, dst, ld, x, ld_x, sps);
+                           ws, wa, M, N, K, dst, ld, x, ld_x, sps, packed);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if (ns > 1) return launch_reduce(part, ns, M, N, aa, wa, out, out_type, ld_out, s);
     return hipSuccess;
+}
+
+// Decode-packed weights: one wave per (16-row group, 128-wide chunk) block;
+// lane l copies the 16 code bytes lane l of a decode wave loads, lanes 0-15
+// the 8 scale bytes of row 16 g + l; rows past N are written as zeros.
+__global__ __launch_bounds__(256) void decode_pack_kernel(const uint8_t *__restrict__ wc,
+                                                          const uint8_t *__restrict__ ws, int64_t N, int64_t K,
+                                                          uint8_t *__restrict__ wp, int64_t blocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t chunks = K >> 7;
+    for (int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); b < blocks; b += (int64_t)gridDim.x * 4) {
+        const int64_t g = b / chunks, c = b - g * chunks;
+        const int64_t row = g * 16 + (lane & 15);
+        uint4 q = make_uint4(0, 0, 0, 0);
+        if (row < N) q = *reinterpret_cast<const uint4 *>(wc + row * (K >> 1) + c * 64 + (lane >> 4) * 16);
+        uint8_t *blk = wp + b * kPackBlock;
+        *reinterpret_cast<uint4 *>(blk + lane * 16) = q;
+        if (lane < 16) {
+            uint2 sc = make_uint2(0, 0);
+            if (row < N) {
+                const uint32_t *sp = reinterpret_cast<const uint32_t *>(ws + row * (K >> 4) + c * 8);
+                sc = make_uint2(sp[0], sp[1]);
+            }
+            *reinterpret_cast<uint2 *>(blk + 1024 + lane * 8) = sc;
+        }
+    }
 }
 
 __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
@@ -723,50 +762,56 @@ hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64
 template <int kA>
 hipError_t launch_f4(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
                      const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                     const DecodePlan &p, int S, float *part, hipStream_t s, const uint16_t *x, int64_t ld_x) {
+                     const DecodePlan &p, int S, float *part, hipStream_t s, const uint16_t *x, int64_t ld_x, int pk) {
     if (p.waves == 4)
         return launch_nvfp4_cfg<1, 1, 4, 2, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
-                                                      x, ld_x);
+                                                      x, ld_x, pk);
     if (p.waves == 8)
         return launch_nvfp4_cfg<1, 1, 8, 2, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
-                                                      x, ld_x);
+                                                      x, ld_x, pk);
     return launch_nvfp4_cfg<1, 1, 16, 1, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
-                                                   x, ld_x);
+                                                   x, ld_x, pk);
 }
 
 template <int MG>
 hipError_t launch_nv_mg(const uint8_t *ac, const uint8_t *as, const float *aa_in, const uint8_t *wc,
                         const uint8_t *ws, const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type,
-                        int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s) {
+                        int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s, int pk) {
     float *aa = const_cast<float *>(aa_in);  // only read when A is NVFP4
     if constexpr (MG == 1)
         if (decode_fp4_form(M, K))
-            return launch_f4<A_NVFP4>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, nullptr, 0);
+            return launch_f4<A_NVFP4>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, nullptr, 0,
+                                      pk);
     if (p.ng == 4 && !p.pipe)
         return launch_nvfp4_cfg<MG, 4, 8, 1, A_NVFP4, false, false>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type,
-                                                                    ld_out, S, part, s);
-    if (p.ng == 4) return launch_nvfp4_cfg<MG, 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+                                                                    ld_out, S, part, s, nullptr, 0, pk);
+    if (p.ng == 4) return launch_nvfp4_cfg<MG, 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                       nullptr, 0, pk);
     if constexpr (MG == 4)
         if (p.ng == 2 && p.waves == 4)
-            return launch_nvfp4_cfg<4, 2, 4, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
-    if (p.ng == 2) return launch_nvfp4_cfg<MG, 2, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+            return launch_nvfp4_cfg<4, 2, 4, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                       nullptr, 0, pk);
+    if (p.ng == 2) return launch_nvfp4_cfg<MG, 2, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                       nullptr, 0, pk);
     if (p.waves == 8)
-        return launch_nvfp4_cfg<MG, 1, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
-    return launch_nvfp4_cfg<MG, 1, 16, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s);
+        return launch_nvfp4_cfg<MG, 1, 8, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                       nullptr, 0, pk);
+    return launch_nvfp4_cfg<MG, 1, 16, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                       nullptr, 0, pk);
 }
 
 template <int kA>
 hipError_t launch_fused_a(const uint16_t *x, int64_t ld_x, float *a_alpha, const uint8_t *wc, const uint8_t *ws,
                           const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
-                          const DecodePlan &p, int S, float *part, hipStream_t s) {
+                          const DecodePlan &p, int S, float *part, hipStream_t s, int pk) {
     if (decode_fp4_form(M, K))
         return launch_f4<kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, x,
-                             ld_x);
+                             ld_x, pk);
     if (p.ng == 2)
         return launch_nvfp4_cfg<1, 2, 8, 1, kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, S,
-                                                part, s, x, ld_x);
+                                                part, s, x, ld_x, pk);
     return launch_nvfp4_cfg<1, 1, 16, 1, kA>(nullptr, nullptr, a_alpha, wc, ws, wa, M, N, K, out, out_type, ld_out, S,
-                                             part, s, x, ld_x);
+                                             part, s, x, ld_x, pk);
 }
 
 }  // namespace
@@ -785,34 +830,47 @@ hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, i
 hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
                                int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
-                               size_t ws_bytes, hipStream_t s) {
+                               size_t ws_bytes, hipStream_t s, bool packed) {
     const DecodePlan p = decode_plan(DECODE_NVFP4, M, N, K);
     const int S = plan_slices(p, M, N, ws, ws_bytes);
     float *part = (float *)ws;
     if (M <= 16)
         return launch_nv_mg<1>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
-                               p, S, part, s);
+                               p, S, part, s, packed);
     if (M <= 32)
         return launch_nv_mg<2>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
-                               p, S, part, s);
+                               p, S, part, s, packed);
     if (M <= 64)
         return launch_nv_mg<4>(a_codes, a_scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
-                               p, S, part, s);
+                               p, S, part, s, packed);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, int dynamic, const uint8_t *w_codes,
                                const uint8_t *w_scales, const float *w_alpha, int64_t M, int64_t N, int64_t K,
-                               void *out, int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s) {
+                               void *out, int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s,
+                               bool packed) {
     if (M > 16 || M * K > kFusedDecodeMaxElems) return hipErrorInvalidValue;
     const DecodePlan p = decode_plan(DECODE_FUSED, M, N, K);
     const int S = plan_slices(p, M, N, ws, ws_bytes);
     float *part = (float *)ws;
     if (dynamic)
         return launch_fused_a<A_BF16_DYNAMIC>(x, ld_x, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type,
-                                              ld_out, p, S, part, s);
+                                              ld_out, p, S, part, s, packed);
     return launch_fused_a<A_BF16_STATIC>(x, ld_x, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out, out_type, ld_out,
-                                         p, S, part, s);
+                                         p, S, part, s, packed);
+}
+
+hipError_t launch_decode_pack(const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, int64_t K,
+                              uint8_t *w_packed, hipStream_t s) {
+    if (N <= 0 || K <= 0) return hipSuccess;
+    if (K % 128 != 0) return hipErrorInvalidValue;
+    const int64_t blocks = ((N + 15) / 16) * (K / 128);
+    int64_t g = (blocks + 3) / 4;
+    if (g > 65536) g = 65536;
+    hipLaunchKernelGGL(decode_pack_kernel, dim3((unsigned)g), dim3(256), 0, s, w_codes, w_scales, N, K, w_packed,
+                       blocks);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void *out, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s) {

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.nvfp4_abi_version() == 2
+    assert L.nvfp4_abi_version() == 3
 
 
 def test_workspace_sizes(L):
@@ -137,3 +137,34 @@ def test_quant_out_dynamic_argument_errors(L):
     assert f(*args, 64, 256, 512, FAKE, FAKE, FAKE, None, 0, None) == NVFP4_EWORKSPACE
     assert f(*args, 64, 256, 512, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1010), need, None) == NVFP4_EINVAL  # alignment
     assert b"256-byte" in L.nvfp4_last_error()
+
+
+def test_decode_packed_argument_errors(L):
+    from nvfp4_prefill_gemm_amd.binding import NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EWORKSPACE, NVFP4_OK
+
+    assert L.nvfp4_decode_pack_size(1000, 4096) == 63 * 32 * 1152
+    assert L.nvfp4_decode_pack_size(1000, 4160) == 0 and L.nvfp4_decode_pack_size(0, 4096) == 0
+    p = L.nvfp4_decode_pack
+    assert p(FAKE, FAKE, 64, 4160, FAKE, None) == NVFP4_EUNSUPPORTED  # K % 128
+    assert b"multiple of 128" in L.nvfp4_last_error()
+    assert p(None, FAKE, 64, 4096, FAKE, None) == NVFP4_EINVAL
+    assert p(FAKE, FAKE, 64, 4096, ctypes.c_void_p(0x1008), None) == NVFP4_EINVAL  # packed alignment
+    assert p(None, None, 0, 4096, None, None) == NVFP4_OK  # empty: no launch
+    g = L.nvfp4_gemm_packed
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert g(*args, 65, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EUNSUPPORTED  # decode batches only
+    assert b"decode batches" in L.nvfp4_last_error()
+    assert g(*args, 8, 64, 4160, FAKE, 0, 64, None, 0, None) == NVFP4_EUNSUPPORTED  # K % 128
+    assert g(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EINVAL  # no weight
+    assert g(*args, 8, 64, 4096, FAKE, 0, 32, None, 0, None) == NVFP4_EINVAL  # ld_out < N
+    assert g(*args, -1, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EINVAL
+    assert g(None, None, None, None, None, 0, 64, 4096, None, 0, 64, None, 0, None) == NVFP4_OK
+    q = L.nvfp4_quant_gemm_packed
+    qa = (FAKE, 4096, FAKE)
+    assert q(*qa, 0, FAKE, FAKE, 65, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EUNSUPPORTED
+    assert q(*qa, 3, FAKE, FAKE, 8, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EINVAL  # alpha mode
+    # batch 32 takes the quantizer into the workspace: without one, EWORKSPACE
+    assert q(*qa, 0, FAKE, FAKE, 32, 4096, 4096, FAKE, 0, 4096, None, 0, None) == NVFP4_EWORKSPACE
+    # one row takes the fused kernel, whose dynamic alpha needs the amax partials
+    assert q(*qa, 0, FAKE, FAKE, 1, 4096, 4096, FAKE, 0, 4096, None, 0, None) == NVFP4_EWORKSPACE
+    assert q((FAKE), 4000, FAKE, 0, FAKE, FAKE, 8, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EINVAL  # ld_x
