@@ -283,6 +283,28 @@ int bf16_gemm(const void *a_bf16, const void *w_bf16, int64_t M, int64_t N, int6
               int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * BF16 decode on decode-packed weights (the decode path of Mix-Quant Section
+ * 3.3 keeps the BF16 weights; decode is bound by moving them, Section 3.1).
+ * The same BF16 values re-laid out once, so that each 16-byte load of a
+ * decode wave reads contiguous memory: for every group of 16 weight rows g
+ * and 32-wide K step t, 1 KB at offset (g * K / 32 + t) * 1024 whose byte
+ * 16 l + b (l = 0..63, b = 0..15) is byte 16 (l / 16) + b of the 64 bytes of
+ * step t in row 16 g + l % 16; rows past N are zeros.
+ *   bf16_decode_pack_size: bytes of the packed weight (0 if N <= 0, K <= 0 or
+ *   K % 32 != 0).
+ *   bf16_decode_pack: w_bf16 [N, K] contiguous (16-byte aligned) -> w_packed
+ *   (16-byte aligned, caller-owned).  K % 32 != 0: NVFP4_EUNSUPPORTED.
+ *   bf16_gemm_packed: bf16_gemm for decode batches (M <= 64; K % 32 == 0,
+ *   K < 2^24, else NVFP4_EUNSUPPORTED) on the packed weight; other arguments
+ *   and the workspace (bf16_gemm_workspace_size) as in bf16_gemm.  Results
+ *   equal bf16_gemm's on the row-major weight bit for bit.
+ */
+size_t bf16_decode_pack_size(int64_t N, int64_t K);
+int bf16_decode_pack(const void *w_bf16, int64_t N, int64_t K, void *w_packed, void *stream);
+int bf16_gemm_packed(const void *a_bf16, const void *w_packed, int64_t M, int64_t N, int64_t K, void *out,
+                     int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * MXFP4 (Mix-Quant Section 3.3 names it as the coarser microscaling format
  * with larger groups and power-of-two scales): E2M1 codes as above and one
  * E8M0 scale byte (value 2^(code - 127)) per 32 consecutive elements, no

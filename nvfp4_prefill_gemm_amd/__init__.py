@@ -11,7 +11,8 @@ def __getattr__(name):
     # the binding imports torch; load it on first use of an entry point
     if name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_quant_gemm", "nvfp4_gemm_quant_out",
                 "nvfp4_gemm_quant_out_dynamic", "nvfp4_decode_pack", "nvfp4_gemm_packed",
-                "nvfp4_quant_gemm_packed", "bf16_gemm", "mxfp4_quantize", "mxfp4_gemm",
+                "nvfp4_quant_gemm_packed", "bf16_gemm", "bf16_decode_pack", "bf16_gemm_packed",
+                "mxfp4_quantize", "mxfp4_gemm",
                 "binding", "lib", "last_error"):
         import importlib
 

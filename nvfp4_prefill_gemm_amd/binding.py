@@ -41,6 +41,9 @@ _SIGNATURES = {
     "nvfp4_gemm_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "nvfp4_quant_gemm_packed": (_I, [_P, _I64, _P, _I, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "bf16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "bf16_decode_pack_size": (_SZ, [_I64, _I64]),
+    "bf16_decode_pack": (_I, [_P, _I64, _I64, _P, _P]),
+    "bf16_gemm_packed": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "bf16_gemm": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "mxfp4_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxfp4_gemm": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I64, _P]),
@@ -545,4 +548,67 @@ def mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out: torch.Tensor | None = 
     rc = lib().mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K, _ptr(out),
                           _OUT[out.dtype], out.stride(0), _stream(stream))
     _check("mxfp4_gemm", rc)
+    return out
+
+
+class Bf16PackedWeight(NamedTuple):
+    """A BF16 weight [N, K] in the decode-packed layout (include/nvfp4.h):
+    ``packed`` uint8 [bf16_decode_pack_size(N, K)]."""
+    packed: torch.Tensor
+    n: int
+    k: int
+
+
+def bf16_decode_pack_size(N: int, K: int) -> int:
+    return int(lib().bf16_decode_pack_size(N, K))
+
+
+def bf16_decode_pack(w: torch.Tensor, packed: torch.Tensor | None = None, stream=None) -> Bf16PackedWeight:
+    """Row-major BF16 weight [N, K] -> the decode-packed layout bf16_gemm_packed
+    streams (K % 32 == 0)."""
+    _mat(w, "w", torch.bfloat16)
+    N, K = w.shape
+    if K % 32:
+        raise ValueError(f"w: K = {K} must be a multiple of 32")
+    if packed is None:
+        packed = torch.empty(bf16_decode_pack_size(N, K), dtype=torch.uint8, device=w.device)
+    wp = _bf16_packed(Bf16PackedWeight(packed, N, K))
+    _same_device(("w", w), ("packed", packed))
+    rc = lib().bf16_decode_pack(_ptr(w), N, K, _ptr(packed), _stream(stream))
+    _check("bf16_decode_pack", rc)
+    return wp
+
+
+def _bf16_packed(wp, K: int | None = None):
+    if not isinstance(wp, Bf16PackedWeight):
+        raise TypeError(f"the weight must be a Bf16PackedWeight, got {type(wp).__name__}")
+    if K is not None and wp.k != K:
+        raise ValueError(f"activations and the packed weight disagree on K ({K} vs {wp.k})")
+    if wp.k % 32:
+        raise ValueError(f"packed weight: K = {wp.k} must be a multiple of 32")
+    _tensor(wp.packed, "packed")
+    if wp.packed.dtype != torch.uint8 or wp.packed.dim() != 1 or not wp.packed.is_contiguous():
+        raise ValueError("packed must be a contiguous 1-D uint8 tensor")
+    if wp.packed.numel() != bf16_decode_pack_size(wp.n, wp.k):
+        raise ValueError(f"packed holds {wp.packed.numel()} bytes, the layout of [{wp.n}, {wp.k}] takes "
+                         f"{bf16_decode_pack_size(wp.n, wp.k)}")
+    return wp
+
+
+def bf16_gemm_packed(a: torch.Tensor, wp: Bf16PackedWeight, out: torch.Tensor | None = None,
+                     out_dtype=torch.bfloat16, workspace=None, stream=None) -> torch.Tensor:
+    """bf16_gemm on a decode-packed weight (M <= 64)."""
+    _mat(a, "a", torch.bfloat16)
+    M, K = a.shape
+    _bf16_packed(wp, K)
+    N = wp.n
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _out(out, "out", M, N)
+    _same_device(("a", a), ("packed", wp.packed), ("out", out),
+                 ("workspace", workspace if isinstance(workspace, torch.Tensor) else None))
+    workspace = _workspace(workspace, bf16_gemm_workspace_size(M, N, K) if workspace is None else 0, a.device)
+    rc = lib().bf16_gemm_packed(_ptr(a), _ptr(wp.packed), M, N, K, _ptr(out), _OUT[out.dtype], out.stride(0),
+                                _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("bf16_gemm_packed", rc)
     return out

@@ -498,4 +498,45 @@ int nvfp4_quant_gemm_packed(const void *x_bf16, int64_t ld_x, float *a_alpha, in
                       "nvfp4 decode kernel");
 }
 
+size_t bf16_decode_pack_size(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % 32 != 0) return 0;
+    return (size_t)((N + 15) / 16) * (size_t)(K / 32) * 1024;
+}
+
+int bf16_decode_pack(const void *w_bf16, int64_t N, int64_t K, void *w_packed, void *stream) {
+    const char *fn = "bf16_decode_pack";
+    if (N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (K % 32 != 0) return fail(NVFP4_EUNSUPPORTED, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (N == 0 || K == 0) return ok();
+    if (!w_bf16 || !w_packed) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
+    if (!aligned(w_bf16, 16) || !aligned(w_packed, 16))
+        return fail(NVFP4_EINVAL, "%s: w and w_packed must be 16-byte aligned", fn);
+    return hip_status(nvfp4::launch_bf16_pack((const uint16_t *)w_bf16, N, K, (uint8_t *)w_packed, as_stream(stream)),
+                      "pack kernel");
+}
+
+int bf16_gemm_packed(const void *a_bf16, const void *w_packed, int64_t M, int64_t N, int64_t K, void *out,
+                     int out_dtype, int64_t ld_out, void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "bf16_gemm_packed";
+    if (M < 0 || N < 0 || K < 0) return fail(NVFP4_EINVAL, "%s: negative size", fn);
+    if (M > nvfp4::kSkinnyMaxM)
+        return fail(NVFP4_EUNSUPPORTED, "%s: M (%lld) above %lld (decode batches only)", fn, (long long)M,
+                    (long long)nvfp4::kSkinnyMaxM);
+    if (K % 32 != 0 || K >= nvfp4::kSkinnyMaxK)
+        return fail(NVFP4_EUNSUPPORTED, "%s: K (%lld) must be a multiple of 32 below 2^24", fn, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    int rc = check_out(out, out_dtype, N, ld_out, fn);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    const int esz = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    if (K == 0) return hip_status(nvfp4::launch_fill_zero(out, M, N, ld_out, esz, s), "fill kernel");
+    if (!a_bf16 || !w_packed) return fail(NVFP4_EINVAL, "%s: null pointer", fn);
+    if (!aligned(a_bf16, 16) || !aligned(w_packed, 16))
+        return fail(NVFP4_EINVAL, "%s: a and w_packed must be 16-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16)) return fail(NVFP4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    return hip_status(nvfp4::launch_skinny_bf16((const uint16_t *)a_bf16, (const uint16_t *)w_packed, M, N, K, out,
+                                                out_dtype, ld_out, workspace, workspace_bytes, s, true),
+                      "bf16 decode kernel");
+}
+
 }  // extern "C"

@@ -104,9 +104,14 @@ inline bool decode_fp4_form(int64_t M, int64_t K) { return M <= 2 && (K & 127) =
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K);
 
 // ws / ws_bytes: the split-K partials; a workspace smaller than
-// decode_workspace_bytes() runs the plan without a split.
+// decode_workspace_bytes() runs the plan without a split.  packed: w is the
+// BF16 decode-packed weight (K % 32 == 0): for 16-row group g and 32-wide K
+// step t, 1 KB at (g * K / 32 + t) * 1024 whose byte 16 l + b is byte
+// 16 (l / 16) + b of row 16 g + l % 16's step t (64 bytes); rows past N zero.
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
-                              int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s);
+                              int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s,
+                              bool packed = false);
+hipError_t launch_bf16_pack(const uint16_t *w, int64_t N, int64_t K, uint8_t *w_packed, hipStream_t s);
 
 // Decode-packed NVFP4 weights (nvfp4_decode_pack): for every group of 16
 // rows g and 128-wide K chunk c, one block of kPackBlock bytes at

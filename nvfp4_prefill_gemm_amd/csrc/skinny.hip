@@ -109,7 +109,7 @@ __device__ __forceinline__ void slice_steps(int64_t steps, int64_t sps, int64_t 
 template <int MG, int NG, int WAVES, int U, int kOut, bool kPipe>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                             int64_t M, int64_t N, int64_t K, void *__restrict__ out,
-                                                            int64_t ld_out, int64_t sps) {
+                                                            int64_t ld_out, int64_t sps, int packed) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = (int64_t)blockIdx.x * (NG * 16);
     const int kq = (lane >> 4) * 8;
@@ -123,13 +123,20 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
         for (int j = 0; j < NG; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
     // buffer resources over this workgroup's weight rows and over X: rows past
-    // N or M and steps past the slice or K read zeros (offset beyond the resource)
+    // N or M and steps past the slice or K read zeros (offset beyond the
+    // resource).  A lane's weight bytes of step ks are at wro + ks * wstep:
+    // row-major W [N, K] (step 64), or the decode-packed blocks (1 KB per 16
+    // rows and step, in lane order; step 1 KB; K % 32 == 0).
     const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
-    const rsrc_t wrs = make_rsrc(w + n0 * K, (uint32_t)(nrows * K * 2));
+    const int64_t gbytes = (K >> 5) * 1024, ngroups = (nrows + 15) >> 4;  // packed bytes per 16-row group
+    const rsrc_t wrs = packed ? make_rsrc(w + (n0 >> 4) * (gbytes >> 1), (uint32_t)(ngroups * gbytes))
+                              : make_rsrc(w + n0 * K, (uint32_t)(nrows * K * 2));
+    const uint32_t wstep = packed ? 1024u : 64u;
     const rsrc_t xrs = make_rsrc(x, (uint32_t)(M * K * 2));
     uint32_t wro[NG], xro[MG];  // byte offsets of this lane's rows
 #pragma unroll
-    for (int j = 0; j < NG; ++j) wro[j] = (uint32_t)((j * 16 + (lane & 15)) * K * 2);
+    for (int j = 0; j < NG; ++j)
+        wro[j] = packed ? (uint32_t)(j * gbytes + lane * 16) : (uint32_t)((j * 16 + (lane & 15)) * K * 2 + kq * 2);
 #pragma unroll
     for (int i = 0; i < MG; ++i) xro[i] = (uint32_t)((i * 16 + (lane & 15)) * K * 2);
 
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t *__re
             const int64_t ks = ks0 + (int64_t)u * WAVES, k = ks * 32 + kq;
             const bool kin = ks < se && k + 8 <= K;
 #pragma unroll
-            for (int j = 0; j < NG; ++j) bw[u][j] = buf_load16(wrs, kin ? wro[j] + (uint32_t)(k * 2) : kBufOOB);
+            for (int j = 0; j < NG; ++j) bw[u][j] = buf_load16(wrs, kin ? wro[j] + (uint32_t)ks * wstep : kBufOOB);
 #pragma unroll
             for (int i = 0; i < MG; ++i) ax[u][i] = buf_load16(xrs, kin ? xro[i] + (uint32_t)(k * 2) : kBufOOB);
         }
@@ -602,7 +609,7 @@ int64_t steps_per_slice(int64_t steps, int S) { return S <= 1 ? (steps > 0 ? ste
 // kPipe: the pinned two-stage loop, else the compiler's schedule.
 template <int MG, int NG, int WAVES, int U, bool kPipe = true>
 hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
-                           int out_type, int64_t ld_out, int S, float *part, hipStream_t s) {
+                           int out_type, int64_t ld_out, int S, float *part, hipStream_t s, int packed) {
     const int64_t nb = (N + NG * 16 - 1) / (NG * 16);
     if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t sps = steps_per_slice((K + 31) >> 5, S);
@@ -610,16 +617,16 @@ hipError_t launch_bf16_cfg(const uint16_t *a, const uint16_t *w, int64_t M, int6
     const dim3 grid((unsigned)nb, (unsigned)ns), block(WAVES * 64);
     if (ns > 1) {
         hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_PARTIAL, kPipe>), grid, block, 0, s, a, w, M, N, K,
-                           (void *)part, N, sps);
+                           (void *)part, N, sps, packed);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         return launch_reduce(part, ns, M, N, nullptr, nullptr, out, out_type, ld_out, s);
     }
     if (out_type == OUT_BF16)
         hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_BF16, kPipe>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
-                           sps);
+                           sps, packed);
     else
         hipLaunchKernelGGL((skinny_kernel<MG, NG, WAVES, U, DOUT_F32, kPipe>), grid, block, 0, s, a, w, M, N, K, out, ld_out,
-                           sps);
+                           sps, packed);
     return hipGetLastError();
 }
 
@@ -687,6 +694,22 @@ __global__ __launch_bounds__(256) void decode_pack_kernel(const uint8_t *__restr
     }
 }
 
+// BF16 decode-packed weights: one wave per (16-row group, 32-wide K step)
+// block of 1 KB; lane l copies the 16 bytes lane l of a decode wave loads
+// (row 16 g + l % 16, elements 32 t + 8 (l / 16) .. + 7); rows past N are zeros.
+__global__ __launch_bounds__(256) void bf16_pack_kernel(const uint16_t *__restrict__ w, int64_t N, int64_t K,
+                                                        uint8_t *__restrict__ wp, int64_t blocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t steps = K >> 5;
+    for (int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); b < blocks; b += (int64_t)gridDim.x * 4) {
+        const int64_t g = b / steps, t = b - g * steps;
+        const int64_t row = g * 16 + (lane & 15);
+        uint4 q = make_uint4(0, 0, 0, 0);
+        if (row < N) q = *reinterpret_cast<const uint4 *>(w + row * K + t * 32 + (lane >> 4) * 8);
+        *reinterpret_cast<uint4 *>(wp + b * 1024 + lane * 16) = q;
+    }
+}
+
 __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
         for (int64_t c = threadIdx.x; c < row_bytes; c += blockDim.x) out[r * ld_bytes + c] = 0;
@@ -748,14 +771,15 @@ int plan_slices(const DecodePlan &p, int64_t M, int64_t N, void *ws, size_t ws_b
 
 template <int MG>
 hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
-                          int out_type, int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s) {
-    if (p.ng == 8) return launch_bf16_cfg<MG, 8, 4, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
-    if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
-    if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
-    if (p.ng == 2) return launch_bf16_cfg<MG, 2, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
+                          int out_type, int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s,
+                          int pk) {
+    if (p.ng == 8) return launch_bf16_cfg<MG, 8, 4, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    if (p.ng == 2) return launch_bf16_cfg<MG, 2, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if constexpr (MG == 1)
-        if (!p.pipe) return launch_bf16_cfg<1, 1, 16, 1, false>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
-    return launch_bf16_cfg<MG, 1, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s);
+        if (!p.pipe) return launch_bf16_cfg<1, 1, 16, 1, false>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    return launch_bf16_cfg<MG, 1, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
 }
 
 // The FP4-MFMA form (M <= 2, K % 128 == 0) of the plans decode_plan gives it.
@@ -817,13 +841,13 @@ hipError_t launch_fused_a(const uint16_t *x, int64_t ld_x, float *a_alpha, const
 }  // namespace
 
 hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, int64_t N, int64_t K, void *out,
-                              int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s) {
+                              int out_type, int64_t ld_out, void *ws, size_t ws_bytes, hipStream_t s, bool packed) {
     const DecodePlan p = decode_plan(DECODE_BF16, M, N, K);
     const int S = plan_slices(p, M, N, ws, ws_bytes);
     float *part = (float *)ws;
-    if (M <= 16) return launch_bf16_mg<1>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s);
-    if (M <= 32) return launch_bf16_mg<2>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s);
-    if (M <= 64) return launch_bf16_mg<4>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s);
+    if (M <= 16) return launch_bf16_mg<1>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s, packed);
+    if (M <= 32) return launch_bf16_mg<2>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s, packed);
+    if (M <= 64) return launch_bf16_mg<4>(a, w, M, N, K, out, out_type, ld_out, p, S, part, s, packed);
     return hipErrorInvalidValue;
 }
 
@@ -870,6 +894,16 @@ hipError_t launch_decode_pack(const uint8_t *w_codes, const uint8_t *w_scales, i
     if (g > 65536) g = 65536;
     hipLaunchKernelGGL(decode_pack_kernel, dim3((unsigned)g), dim3(256), 0, s, w_codes, w_scales, N, K, w_packed,
                        blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_bf16_pack(const uint16_t *w, int64_t N, int64_t K, uint8_t *w_packed, hipStream_t s) {
+    if (N <= 0 || K <= 0) return hipSuccess;
+    if (K % 32 != 0) return hipErrorInvalidValue;
+    const int64_t blocks = ((N + 15) / 16) * (K / 32);
+    int64_t g = (blocks + 3) / 4;
+    if (g > 65536) g = 65536;
+    hipLaunchKernelGGL(bf16_pack_kernel, dim3((unsigned)g), dim3(256), 0, s, w, N, K, w_packed, blocks);
     return hipGetLastError();
 }
 

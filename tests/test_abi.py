@@ -168,3 +168,22 @@ def test_decode_packed_argument_errors(L):
     # one row takes the fused kernel, whose dynamic alpha needs the amax partials
     assert q(*qa, 0, FAKE, FAKE, 1, 4096, 4096, FAKE, 0, 4096, None, 0, None) == NVFP4_EWORKSPACE
     assert q((FAKE), 4000, FAKE, 0, FAKE, FAKE, 8, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EINVAL  # ld_x
+
+
+def test_bf16_packed_argument_errors(L):
+    from nvfp4_prefill_gemm_amd.binding import NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_OK
+
+    assert L.bf16_decode_pack_size(1000, 4096) == 63 * 128 * 1024
+    assert L.bf16_decode_pack_size(1000, 4104) == 0
+    p = L.bf16_decode_pack
+    assert p(FAKE, 64, 4104, FAKE, None) == NVFP4_EUNSUPPORTED  # K % 32
+    assert p(None, 64, 4096, FAKE, None) == NVFP4_EINVAL
+    assert p(FAKE, 64, 4096, ctypes.c_void_p(0x1008), None) == NVFP4_EINVAL
+    assert p(None, 0, 4096, None, None) == NVFP4_OK
+    g = L.bf16_gemm_packed
+    assert g(FAKE, FAKE, 65, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EUNSUPPORTED
+    assert g(FAKE, FAKE, 8, 64, 4104, FAKE, 0, 64, None, 0, None) == NVFP4_EUNSUPPORTED
+    assert g(FAKE, None, 8, 64, 4096, FAKE, 0, 64, None, 0, None) == NVFP4_EINVAL
+    assert g(FAKE, FAKE, 8, 64, 4096, FAKE, 0, 32, None, 0, None) == NVFP4_EINVAL  # ld_out
+    assert g(FAKE, FAKE, 8, 64, 4096, FAKE, 0, 64, ctypes.c_void_p(0x1008), 4096, None) == NVFP4_EINVAL
+    assert g(None, None, 0, 64, 4096, None, 0, 64, None, 0, None) == NVFP4_OK

@@ -30,6 +30,25 @@ def test_layout_places_known_bytes():
     assert p.size == 3 * 2 * ref.BLOCK
 
 
+@pytest.mark.parametrize("N,K", [(1, 32), (16, 64), (21, 96), (40, 256)])
+def test_bf16_reshaped_layout_equals_definition(N, K):
+    g = np.random.default_rng(N * 100 + K)
+    w = g.integers(0, 65536, size=(N, K), dtype=np.uint16)
+    assert np.array_equal(ref.pack_bf16(w), ref.pack_bf16_loops(w))
+
+
+def test_bf16_layout_places_known_bytes():
+    """Row 18 (group 1, r = 2), element 45 (step 1, quarter 1, element 5):
+    lane 16 + 2, bytes 10 and 11 of its 16."""
+    N, K = 20, 64
+    w = np.zeros((N, K), dtype=np.uint16)
+    w[18, 45] = 0xBEEF
+    p = ref.pack_bf16(w)
+    base = (1 * 2 + 1) * ref.BF16_BLOCK
+    assert p[base + 16 * 18 + 10] == 0xEF and p[base + 16 * 18 + 11] == 0xBE
+    assert np.count_nonzero(p) == 2 and p.size == 2 * 2 * ref.BF16_BLOCK
+
+
 @pytest.fixture(scope="module")
 def nvb():
     from nvfp4_prefill_gemm_amd import binding
@@ -47,6 +66,12 @@ def test_pack_size_matches_layout(nvb):
     for N, K in ((1, 128), (40, 256), (1000, 4096), (24576, 4096), (4096, 12288)):
         assert nvb.decode_pack_size(N, K) == ((N + 15) // 16) * (K // 128) * ref.BLOCK
     assert nvb.decode_pack_size(0, 128) == 0 and nvb.decode_pack_size(16, 96) == 0
+
+
+def test_bf16_pack_size_matches_layout(nvb):
+    for N, K in ((1, 32), (40, 256), (24576, 4096), (4096, 12288)):
+        assert nvb.bf16_decode_pack_size(N, K) == ((N + 15) // 16) * (K // 32) * ref.BF16_BLOCK
+    assert nvb.bf16_decode_pack_size(16, 40) == 0
 
 
 def test_binding_rejects_malformed_packed_weights(nvb):
@@ -70,3 +95,12 @@ def test_binding_rejects_malformed_packed_weights(nvb):
         nvb.nvfp4_quant_gemm_packed(torch.zeros((2, 384), dtype=torch.bfloat16), good)
     with pytest.raises(ValueError):  # host tensors
         nvb.nvfp4_quant_gemm_packed(x, good)
+    bwp = nvb.Bf16PackedWeight(torch.zeros(nvb.bf16_decode_pack_size(40, 256), dtype=torch.uint8), 40, 256)
+    with pytest.raises(TypeError):
+        nvb.bf16_gemm_packed(x, good)
+    with pytest.raises(ValueError):  # K disagrees
+        nvb.bf16_gemm_packed(torch.zeros((2, 288), dtype=torch.bfloat16), bwp)
+    with pytest.raises(ValueError):  # K % 32
+        nvb.bf16_decode_pack(torch.zeros((4, 40), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):  # host tensors
+        nvb.bf16_gemm_packed(x, bwp)

@@ -135,3 +135,39 @@ def test_quant_gemm_packed_workspace_errors(nv):
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.nvfp4_quant_gemm_packed(x, wp, workspace=small)
     assert e.value.code == nv.NVFP4_EWORKSPACE
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (40, 96), (1000, 4128), (6144, 4096)])
+def test_bf16_pack_bytes(nv, N, K):
+    g = np.random.default_rng(N * 3 + K)
+    w = g.integers(0, 65536, size=(N, K), dtype=np.uint16)
+    say("bf16 decode pack", N, K)
+    wp = nv.bf16_decode_pack(bf16_dev(w))
+    assert wp.n == N and wp.k == K
+    assert np.array_equal(host(wp.packed), decode_pack_ref.pack_bf16(w))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 33, 32), (1, 6144, 4096), (1, 4096, 12288), (2, 1000, 4128), (8, 6144, 4096),
+                                   (8, 4096, 4096), (16, 300, 1056), (17, 300, 4096), (33, 520, 12288),
+                                   (64, 24576, 4096), (64, 4096, 12288), (64, 6144, 4096), (48, 6200, 4160)])
+def test_bf16_gemm_packed_equals_row_major(nv, oracle_mod, M, N, K):
+    """bf16_gemm_packed == bf16_gemm bit for bit (FP32 and BF16 out, with the
+    split-K workspace and without); the FP32 output within the gate of the
+    oracle's BF16 product."""
+    import torch
+
+    g = np.random.default_rng(M * 11 + N + K)
+    a = wl.activations(M, K, g)
+    wt = wl.weights(N, K, g)
+    x, w = bf16_dev(a), bf16_dev(wt)
+    say("bf16 gemm packed vs row-major", M, N, K)
+    wp = nv.bf16_decode_pack(w)
+    for ws in (None, False):
+        for od in (torch.float32, torch.bfloat16):
+            y_rm = nv.bf16_gemm(x, w, out_dtype=od, workspace=ws)
+            y_pk = nv.bf16_gemm_packed(x, wp, out_dtype=od, workspace=ws)
+            assert torch.equal(y_pk, y_rm), f"packed differs from row-major ({od}, workspace {ws})"
+    if M * N * K <= 64 * 6144 * 4096:
+        y = nv.bf16_gemm_packed(x, wp, out_dtype=torch.float32)
+        parity.assert_gemm_close(host(y), oracle_mod.bf16_gemm(a, wt), parity.GEMM_TOL_F32,
+                                 f"bf16 packed {M}x{N}x{K}")
