@@ -538,8 +538,11 @@ def _decode(nv, wl, layers, s, e):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / n * 1e3
 
-    # BF16 decode GEMMs (the method's decode precision): two weight copies
+    # BF16 decode GEMMs (the method's decode precision): two weight copies,
+    # decode-packed (bf16_decode_pack, once at load); the row-major weights'
+    # step is timed beside it
     copies = [[L["w_bf16"] for L in layers], [L["w_bf16"].clone() for L in layers]]
+    packed = [[nv.bf16_decode_pack(w) for w in cp] for cp in copies]
     decode = {}
     for Md in wl.PHASE_SPLIT_DECODE_M:
         xs = [torch.randn((Md, L["K"]), device=dev).to(torch.bfloat16) for L in layers]
@@ -549,20 +552,30 @@ def _decode(nv, wl, layers, s, e):
 
         def dec_step(c):
             for i, L in enumerate(layers):
+                nv.bf16_gemm_packed(xs[i], packed[c][i], out=ys[i], workspace=wsd[i])
+
+        def dec_step_row_major(c):
+            for i, L in enumerate(layers):
                 nv.bf16_gemm(xs[i], copies[c][i], out=ys[i], workspace=wsd[i])
         us = graph_us(dec_step, 2, 20)
+        us_rm = graph_us(dec_step_row_major, 2, 20)
         nbytes = sum(2 * L["N"] * L["K"] + 2 * Md * L["K"] + 2 * Md * L["N"] for L in layers)
         decode[str(Md)] = {"us_per_step": round(us, 1), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
-                           "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3)}
+                           "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3),
+                           "weights": "decode-packed", "row_major_us_per_step": round(us_rm, 1)}
     out["decode_bf16"] = decode
-    del copies
+    del copies, packed
 
     # NVFP4 x NVFP4 decode (the uniform-NVFP4 / FP4-decode ablation variants):
     # dynamic-alpha activation quantizer + decode GEMM per layer; a step's
     # NVFP4 weights (109 MB) fit the Infinity Cache, so four copies rotate.
+    # The step runs on decode-packed weights (nvfp4_decode_pack, packed once
+    # like the offline quantization); the row-major weights' step is timed
+    # beside it.
     wq = [[(L["wc"], L["ws"], L["wa"]) for L in layers]]
     for _ in range(3):
         wq.append([(L["wc"].clone(), L["ws"].clone(), L["wa"]) for L in layers])
+    wpk = [[nv.nvfp4_decode_pack(*w) for w in cp] for cp in wq]
     dec4 = {}
     for Md in wl.PHASE_SPLIT_DECODE_M:
         xs = [torch.randn((Md, L["K"]), device=dev).to(torch.bfloat16) for L in layers]
@@ -580,16 +593,23 @@ def _decode(nv, wl, layers, s, e):
         def dec4_step(c):
             for i, L in enumerate(layers):
                 aal, wsb = qa[i]
+                nv.nvfp4_quant_gemm_packed(xs[i], wpk[c][i], a_alpha=aal, out=ys[i], workspace=wsb)
+
+        def dec4_step_row_major(c):
+            for i, L in enumerate(layers):
+                aal, wsb = qa[i]
                 nv.nvfp4_quant_gemm(xs[i], *wq[c][i], a_alpha=aal, out=ys[i], workspace=wsb)
         us = graph_us(dec4_step, 4, 20)
+        us_rm = graph_us(dec4_step_row_major, 4, 20)
         nbytes = sum(L["N"] * L["K"] * 9 // 16 + 2 * Md * L["K"] + Md * L["K"] * 9 // 16 + 2 * Md * L["N"]
                      for L in layers)
         dec4[str(Md)] = {"us_per_step": round(us, 1), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                          "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3),
                          "speedup_vs_bf16_decode": round(decode[str(Md)]["us_per_step"] / us, 3),
+                         "weights": "decode-packed", "row_major_us_per_step": round(us_rm, 1),
                          "fused_layers": [L["name"] for L, f in zip(layers, fused) if f]}
     out["decode_nvfp4"] = dec4
-    del wq
+    del wq, wpk
     return out
 
 

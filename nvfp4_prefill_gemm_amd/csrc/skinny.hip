@@ -728,7 +728,10 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
     // own sweep (fused and unfused, batch 1 and 2): narrower strips and fewer
     // waves than the FP16-expansion form, two chunks per register stage
     if (kind != DECODE_BF16 && decode_fp4_form(M, K)) {
-        if (N >= 16384) return {1, 4, 2, 1};
+        // wide layers: two 16-row groups per workgroup (gate_up on
+        // decode-packed weights, fused batch 1: 15.5 -> 14.0 us; the K
+        // order, set by waves and chunks per stage, is unchanged)
+        if (N >= 16384) return {2, 4, 2, 1};
         if (K >= 8192) return {1, 16, 1, 1};
         return {1, 8, 2, 1};
     }
@@ -737,6 +740,9 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
     // 13.6 / 8.2 / 21.4 us against 13.9 / 8.9 / 23.8 with the pinned loop)
     // and 4 x 4 NVFP4 tiles split over K (down at batch 64: 24.8 against 26.9)
     if (kind == DECODE_BF16) {
+        // 6144-16383 columns at batch <= 16: 32-column strips of 4 waves, four
+        // steps per stage (qkv on decode-packed weights, batch 1: 12.6 -> 11.1 us)
+        if (M <= 16 && N >= 6144 && N < 16384) return {2, 4, 4, 1};
         if (M <= 4) return {1, 16, 1, 1, false};
         if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1, false};
         // wide layers at batch 33-64: 128-column strips read the batch once
@@ -776,6 +782,8 @@ hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64
     if (p.ng == 8) return launch_bf16_cfg<MG, 8, 4, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    if constexpr (MG == 1)
+        if (p.ng == 2 && p.waves == 4) return launch_bf16_cfg<1, 2, 4, 4>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if (p.ng == 2) return launch_bf16_cfg<MG, 2, 16, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if constexpr (MG == 1)
         if (!p.pipe) return launch_bf16_cfg<1, 1, 16, 1, false>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
@@ -787,6 +795,9 @@ template <int kA>
 hipError_t launch_f4(const uint8_t *ac, const uint8_t *as, float *aa, const uint8_t *wc, const uint8_t *ws,
                      const float *wa, int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out,
                      const DecodePlan &p, int S, float *part, hipStream_t s, const uint16_t *x, int64_t ld_x, int pk) {
+    if (p.waves == 4 && p.ng == 2)
+        return launch_nvfp4_cfg<1, 2, 4, 2, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                      x, ld_x, pk);
     if (p.waves == 4)
         return launch_nvfp4_cfg<1, 1, 4, 2, kA, true>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
                                                       x, ld_x, pk);
