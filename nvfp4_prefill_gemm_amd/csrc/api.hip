@@ -108,11 +108,9 @@ int quantize_impl(const char *fn, const void *x_bf16, int64_t rows, int64_t cols
         if (!workspace || workspace_bytes < need)
             return fail(NVFP4_EWORKSPACE, "%s: dynamic alpha needs %zu workspace bytes", fn, need);
         if (!aligned(workspace, 4)) return fail(NVFP4_EINVAL, "%s: workspace is misaligned", fn);
-        if (!nvfp4::quantize_self_amax(rows, cols))
-            if (int rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, rows, cols, ld_x,
-                                                                (uint32_t *)workspace, nparts, s),
-                                    "amax kernel"))
-                return rc;
+        return hip_status(nvfp4::launch_quantize_dynamic((const uint16_t *)x_bf16, rows, cols, ld_x, codes, scales,
+                                                         alpha, (uint32_t *)workspace, nparts, s),
+                          "quantize kernel");
     }
     return hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, rows, cols, ld_x, codes, scales, alpha, dyn,
                                              (const uint32_t *)workspace, nparts, s),
@@ -293,13 +291,10 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
     if (workspace && workspace_bytes >= l.split) {
         uint8_t *codes = wsb + l.codes, *scales = wsb + l.scales;
         const int nparts = nvfp4::amax_parts(M, K);
-        if (dyn && !nvfp4::quantize_self_amax(M, K) &&
-            (rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, M, K, ld_x,
-                                                         (uint32_t *)(wsb + l.parts), nparts, s),
-                             "amax kernel")))
-            return rc;
-        if ((rc = hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha, dyn,
-                                                    (const uint32_t *)(wsb + l.parts), nparts, s),
+        if ((rc = hip_status(dyn ? nvfp4::launch_quantize_dynamic((const uint16_t *)x_bf16, M, K, ld_x, codes, scales,
+                                                                  a_alpha, (uint32_t *)(wsb + l.parts), nparts, s)
+                                 : nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha,
+                                                          0, nullptr, nparts, s),
                              "quantize kernel")))
             return rc;
         if (decode_shape(M, K, 32))
@@ -484,13 +479,10 @@ int nvfp4_quant_gemm_packed(const void *x_bf16, int64_t ld_x, float *a_alpha, in
     uint8_t *wsb = (uint8_t *)workspace;
     uint8_t *codes = wsb + l.codes, *scales = wsb + l.scales;
     const int nparts = nvfp4::amax_parts(M, K);
-    if (dyn && !nvfp4::quantize_self_amax(M, K) &&
-        (rc = hip_status(nvfp4::launch_amax_partials((const uint16_t *)x_bf16, M, K, ld_x,
-                                                     (uint32_t *)(wsb + l.parts), nparts, s),
-                         "amax kernel")))
-        return rc;
-    if ((rc = hip_status(nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha, dyn,
-                                                (const uint32_t *)(wsb + l.parts), nparts, s),
+    if ((rc = hip_status(dyn ? nvfp4::launch_quantize_dynamic((const uint16_t *)x_bf16, M, K, ld_x, codes, scales,
+                                                              a_alpha, (uint32_t *)(wsb + l.parts), nparts, s)
+                             : nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha, 0,
+                                                      nullptr, nparts, s),
                          "quantize kernel")))
         return rc;
     return hip_status(nvfp4::launch_skinny_nvfp4(codes, scales, a_alpha, w_packed, nullptr, w_alpha, M, N, K, out,

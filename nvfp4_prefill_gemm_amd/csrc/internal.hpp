@@ -41,6 +41,12 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials,
                            int nparts, hipStream_t s);
 
+// Dynamic-alpha quantization: the single launch of quantize_self_amax()
+// tensors, else the amax pass into partials (amax_parts(rows, cols) = nparts
+// entries) and the quantize pass.
+hipError_t launch_quantize_dynamic(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                                   uint8_t *scales, float *alpha, uint32_t *partials, int nparts, hipStream_t s);
+
 // Device address and size of this device's scratch array for the amax
 // partials of nvfp4_quantize_noalloc (looked up once per device).
 hipError_t quantize_scratch(uint32_t **ptr, size_t *bytes);

@@ -146,23 +146,20 @@ __device__ __forceinline__ uint32_t tensor_amax_bits(const uint16_t *__restrict_
 }
 static_assert(kSelfLoads * kThreads * 8 >= kSelfAmaxMaxElems, "the single-launch amax reads the whole tensor");
 
-template <int kAlpha>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__restrict__ x, int64_t rows,
-                                                            int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
-                                                            uint8_t *__restrict__ scales, float *__restrict__ alpha_io,
-                                                            const uint32_t *__restrict__ partials, int nparts) {
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // 32-bit item arithmetic: the host guarantees items < 2^31 and cols < 2^30
-    const uint32_t octs = (uint32_t)(cols >> 3);  // 8-element groups per row; even, so pairs never straddle rows
-    const uint32_t nseg = (octs + kSeg - 1) / kSeg;
-    const uint32_t items = (uint32_t)rows * nseg, nw = gridDim.x * kWaves;
-    // Every item is one wave's (row, segment): buffer resources over that row
-    // of X, codes and scales (empty past the last item) turn out-of-range
-    // loads into zeros and drop out-of-range stores, without branches.
-    // Lane l of an item owns whole 16-element blocks: elements
-    // seg * 2048 + j * 1024 + 16 l .. + 16 for j = 0, 1 (two 16-byte loads each).
-    auto load_item = [&](uint32_t it, uint4 *v) __attribute__((always_inline)) {
+// Work items of the quantize pass: item it is one wave's (row, segment) of
+// kSeg octets; lane l owns whole 16-element blocks, elements
+// seg * 2048 + j * 1024 + 16 l .. + 16 for j = 0, 1 (two 16-byte loads each).
+// Buffer resources over that row of X, codes and scales (empty past the last
+// item) turn out-of-range loads into zeros and drop out-of-range stores,
+// without branches.  32-bit item arithmetic: the host guarantees
+// items < 2^31 and cols < 2^30.
+struct QItems {
+    const uint16_t *x;
+    uint8_t *codes, *scales;
+    int64_t cols, ld;
+    uint32_t nseg, items, lane;
+
+    __device__ __forceinline__ void load(uint32_t it, uint4 *v) const {
         const bool ok = it < items;
         const uint32_t r = ok ? it / nseg : 0u, e0 = (it - r * nseg) * (kSeg * 8) + lane * 16u;
         const rsrc_t xs = make_rsrc(x + (int64_t)r * ld, ok ? (uint32_t)cols * 2u : 0u);
@@ -171,49 +168,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
             v[2 * j] = buf_load16(xs, (e0 + 1024u * j) * 2u);
             v[2 * j + 1] = buf_load16(xs, (e0 + 1024u * j) * 2u + 16u);
         }
-    };
-    uint32_t it = blockIdx.x * kWaves + wave;
-    // the tensor scale's inputs are read first, then the first item's loads
-    // are issued, so waiting for the former leaves the latter in flight
-    // (nparts <= kMaxParts: at most kMaxParts / kThreads partials per thread,
-    // loaded without branches; entries past nparts read as zero)
-    constexpr int kPartsPerThread = kMaxParts / kThreads;
-    uint32_t pv[kPartsPerThread];
-    if (kAlpha == ALPHA_PARTIALS) {
-        const rsrc_t ps = make_rsrc(partials, (uint32_t)nparts * 4u);
-#pragma unroll
-        for (int j = 0; j < kPartsPerThread; ++j)
-            pv[j] = __builtin_amdgcn_raw_buffer_load_b32(ps, (threadIdx.x + j * kThreads) * 4u, 0, 0);
     }
-    const float alpha_in = kAlpha == ALPHA_STATIC ? *alpha_io : 0.0f;
-    asm volatile("" ::: "memory");
-    uint4 va[2 * kBlk], vb[2 * kBlk];
-    load_item(it, va);
-    float alpha = alpha_in;
-    if (kAlpha != ALPHA_STATIC) {
-        uint32_t pmax = 0;
-        if constexpr (kAlpha == ALPHA_PARTIALS) {
-#pragma unroll
-            for (int j = 0; j < kPartsPerThread; ++j) pmax = max(pmax, pv[j]);
-        } else {
-            pmax = tensor_amax_bits(x, (uint32_t)rows, octs, ld);
-        }
-        alpha = alpha_from_max(pmax);
-        if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_io = alpha;
-    }
-    const float t = alpha * kQmax;
-    const float rt = t > 0.0f ? div_rn(1.0f, t) : 0.0f;
-    // Per E4M3 scale code: the divisor d = fl32(alpha * sigma), RN(1/d), and
-    // the largest |x| the fast path of quant8_fast takes (-1 when d is
-    // outside [2^-90, 2^100], zero included, so those blocks take quant8).
-    __shared__ float4 dtab[128];
-    if (threadIdx.x < 128) {
-        const float d = alpha * e4m3_decode(threadIdx.x);
-        const bool in = d >= 0x1p-90f && d <= 0x1p100f;
-        dtab[threadIdx.x] = make_float4(d, in ? div_rn(1.0f, d) : 0.0f, in ? d * 0x1p120f : -1.0f, 0.0f);
-    }
-    lds_barrier();
-    auto quant_item = [&](uint32_t it, const uint4 *v) __attribute__((always_inline)) {
+
+    // Eq. 3 against t = alpha * 6 (rt = RN(1/t)), Eq. 2 through the divisor
+    // table, codes and scale bytes stored
+    __device__ __forceinline__ void quant(uint32_t it, const uint4 *v, float t, float rt, const float4 *dtab) const {
         const bool ok = it < items;
         const uint32_t r = ok ? it / nseg : 0u, e0 = (it - r * nseg) * (kSeg * 8) + lane * 16u;
         const rsrc_t cs = make_rsrc(codes + (int64_t)r * (cols >> 1), ok ? (uint32_t)(cols >> 1) : 0u);
@@ -240,16 +199,76 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
             buf_store8(lo, hi, cs, el >> 1);
             buf_store1(code, ss, el >> 4);
         }
-    };
+    }
+};
+
+// Per E4M3 scale code: the divisor d = fl32(alpha * sigma), RN(1/d), and
+// the largest |x| the fast path of quant8_fast takes (-1 when d is outside
+// [2^-90, 2^100], zero included, so those blocks take quant8); threads 0-127
+// fill one entry each, the caller's LDS barrier follows.
+__device__ __forceinline__ void fill_dtab(float4 *dtab, float alpha) {
+    if (threadIdx.x < 128) {
+        const float d = alpha * e4m3_decode(threadIdx.x);
+        const bool in = d >= 0x1p-90f && d <= 0x1p100f;
+        dtab[threadIdx.x] = make_float4(d, in ? div_rn(1.0f, d) : 0.0f, in ? d * 0x1p120f : -1.0f, 0.0f);
+    }
+}
+
+template <int kAlpha>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales, float *__restrict__ alpha_io,
+                                                            const uint32_t *__restrict__ partials, int nparts) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // 32-bit item arithmetic: the host guarantees items < 2^31 and cols < 2^30
+    const uint32_t octs = (uint32_t)(cols >> 3);  // 8-element groups per row; even, so pairs never straddle rows
+    const uint32_t nseg = (octs + kSeg - 1) / kSeg;
+    const uint32_t items = (uint32_t)rows * nseg, nw = gridDim.x * kWaves;
+    const QItems qi{x, codes, scales, cols, ld, nseg, items, lane};
+    uint32_t it = blockIdx.x * kWaves + wave;
+    // the tensor scale's inputs are read first, then the first item's loads
+    // are issued, so waiting for the former leaves the latter in flight
+    // (nparts <= kMaxParts: at most kMaxParts / kThreads partials per thread,
+    // loaded without branches; entries past nparts read as zero)
+    constexpr int kPartsPerThread = kMaxParts / kThreads;
+    uint32_t pv[kPartsPerThread];
+    if (kAlpha == ALPHA_PARTIALS) {
+        const rsrc_t ps = make_rsrc(partials, (uint32_t)nparts * 4u);
+#pragma unroll
+        for (int j = 0; j < kPartsPerThread; ++j)
+            pv[j] = __builtin_amdgcn_raw_buffer_load_b32(ps, (threadIdx.x + j * kThreads) * 4u, 0, 0);
+    }
+    const float alpha_in = kAlpha == ALPHA_STATIC ? *alpha_io : 0.0f;
+    asm volatile("" ::: "memory");
+    uint4 va[2 * kBlk], vb[2 * kBlk];
+    qi.load(it, va);
+    float alpha = alpha_in;
+    if (kAlpha != ALPHA_STATIC) {
+        uint32_t pmax = 0;
+        if constexpr (kAlpha == ALPHA_PARTIALS) {
+#pragma unroll
+            for (int j = 0; j < kPartsPerThread; ++j) pmax = max(pmax, pv[j]);
+        } else {
+            pmax = tensor_amax_bits(x, (uint32_t)rows, octs, ld);
+        }
+        alpha = alpha_from_max(pmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_io = alpha;
+    }
+    const float t = alpha * kQmax;
+    const float rt = t > 0.0f ? div_rn(1.0f, t) : 0.0f;
+    __shared__ float4 dtab[128];
+    fill_dtab(dtab, alpha);
+    lds_barrier();
     // two register stages: the next item's loads are in flight while this
     // one is quantized
     for (;;) {
-        load_item(it + nw, vb);
-        quant_item(it, va);
+        qi.load(it + nw, vb);
+        qi.quant(it, va, t, rt, dtab);
         it += nw;
         if (it >= items) break;
-        load_item(it + nw, va);
-        quant_item(it, vb);
+        qi.load(it + nw, va);
+        qi.quant(it, vb, t, rt, dtab);
         it += nw;
         if (it >= items) break;
     }
@@ -326,6 +345,14 @@ hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, i
 }
 
 bool quantize_self_amax(int64_t rows, int64_t cols) { return rows * cols <= kSelfAmaxMaxElems; }
+
+hipError_t launch_quantize_dynamic(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                                   uint8_t *scales, float *alpha, uint32_t *partials, int nparts, hipStream_t s) {
+    if (quant_items(rows, cols) >= (int64_t(1) << 31) || cols >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+    if (!quantize_self_amax(rows, cols))
+        if (hipError_t e = launch_amax_partials(x, rows, cols, ld, partials, nparts, s); e != hipSuccess) return e;
+    return launch_quantize(x, rows, cols, ld, codes, scales, alpha, 1, partials, nparts, s);
+}
 
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials, int nparts,
