@@ -184,3 +184,20 @@ def test_student_t_long_prefill_full_tensor(nv, oracle_mod):
     xb = wl.activations(w.M, K, wl.rng(w.config_id, 3, 0), w.act_dist)
     say("quantize student-t m32768 down-proj input", xb.shape)
     _assert_same(_gpu_quant(nv, xb), oracle_mod.quantize(xb), "student-t 32768x12288")
+
+
+@pytest.mark.parametrize("rows,cols,ld_pad", [(8, 12288, 0), (32, 4096, 0), (33, 4096, 0), (17, 4112, 24),
+                                              (3, 40960, 8)])
+def test_decode_batch_sizes_amax_placement(nv, oracle_mod, rows, cols, ld_pad):
+    """Decode-batch-sized tensors past the single-launch limit (amax pass +
+    quantize pass, few workgroups), strided rows: the largest magnitude placed
+    in the last row's tail, then in the first row, so every workgroup's
+    partial maximum must count."""
+    g = np.random.default_rng(rows * 7 + cols)
+    x = g.standard_normal((rows, cols), dtype=np.float32)
+    for where in ((rows - 1, cols - 3), (0, 1)):
+        xx = x.copy()
+        xx[where] = 97.0
+        xb = wl.to_bf16_bits(xx)
+        say("quantize decode-batch sizes", rows, cols, ld_pad, where)
+        _assert_same(_gpu_quant(nv, xb, ld=cols + ld_pad), oracle_mod.quantize(xb), f"{rows}x{cols} max at {where}")
