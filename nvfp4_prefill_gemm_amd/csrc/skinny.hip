@@ -41,6 +41,14 @@
 // runs the loop above with the activation codes read from LDS.  Codes, scales
 // and the summation order equal those of quantize followed by the decode GEMM
 // with the same slicing, so the two paths agree bit for bit.
+//
+// Weight layouts: row-major as above, or decode-packed (made once by the
+// pack kernels below): each 16-row group's K chunk (128 wide for NVFP4, with
+// its scales; 32 wide for BF16) stored as one contiguous block in the order
+// the decode lanes load it, so each 16-byte-per-lane load instruction reads
+// 1 KB of consecutive bytes instead of 64 bytes from each of 16 rows.  Only
+// the weight offsets differ (a per-chunk stride), so both layouts give the
+// same results bit for bit.
 #include <stdlib.h>
 #include <string.h>
 
