@@ -7,7 +7,9 @@
  * one FP8 E4M3 scale per 16 consecutive elements along the GEMM reduction
  * dimension K, and one FP32 tensor scale alpha (Eq. 2, Eq. 3).
  *
- * Layouts (all row-major, all in device memory owned by the caller):
+ * Layouts (row-major, except the decode-packed weights described with
+ * nvfp4_decode_pack and bf16_decode_pack; all in device memory owned by the
+ * caller):
  *   BF16 matrix X [rows, cols], row stride ld (elements, >= cols)
  *   codes  uint8 [rows, cols/2]   two E2M1 codes per byte, even element in
  *                                  the low nibble, sign in bit 3 of a nibble
