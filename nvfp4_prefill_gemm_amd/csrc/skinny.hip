@@ -52,6 +52,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -731,6 +733,23 @@ __global__ void fill_zero_kernel(uint8_t *out, int64_t rows, int64_t row_bytes, 
 // rotated weights).  Batches up to 16 are fastest unsplit; larger ones split
 // K so that narrow layers still give about 256 workgroups of wide strips
 // (BF16), or, for NVFP4 whose weights are 3.6x smaller, only on long K.
+// Strip width (16-column groups) among `cands` whose s * ceil(N / (16 ng))
+// workgroups best fill whole rounds of one workgroup per CU on the 256 CUs of
+// an MI355X (ties: the wider strip, which re-reads the batch less often).
+static int fill_ng(int64_t N, int s, std::initializer_list<int> cands) {
+    int best = 0;
+    double best_fill = -1.0;
+    for (int ng : cands) {
+        const int64_t wgs = s * ((N + 16 * ng - 1) / (16 * ng)), rounds = (wgs + 255) / 256;
+        const double fill = (double)wgs / (double)(rounds * 256);
+        if (fill > best_fill + 1e-9 || (fill > best_fill - 1e-9 && ng > best)) {
+            best = ng;
+            best_fill = fill;
+        }
+    }
+    return best;
+}
+
 DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
     // the FP4-MFMA form of the NVFP4 kernel (M <= 2, K % 128 == 0), from its
     // own sweep (fused and unfused, batch 1 and 2): narrower strips and fewer
@@ -753,20 +772,27 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
         if (M <= 16 && N >= 6144 && N < 16384) return {2, 4, 4, 1};
         if (M <= 4) return {1, 16, 1, 1, false};
         if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1, false};
-        // wide layers at batch 33-64: 128-column strips read the batch once
-        // per 128 columns instead of per 64 (gate_up at batch 64: 77.9 -> 69.8 us)
-        if (M > 32 && N >= 16384) return {8, 4, 1, 1};
+        // wide layers at batch 33-64: wide strips read the batch once per 64-128
+        // columns (gate_up at batch 64: 77.9 -> 69.8 us with 128-column strips
+        // instead of 64), and a width that fills whole rounds of the CUs
+        // (96 columns, 256 workgroups for gate_up on decode-packed weights:
+        // 52.0 -> 46.8 us)
+        if (M > 32 && N >= 16384) return {fill_ng(N, 1, {4, 6, 8}), 4, 1, 1};
         const int ng = N >= 6144 || M > 32 ? 4 : 2;
         const int64_t nb = (N + 16 * ng - 1) / (16 * ng);
         const int s = nb <= 64 ? 4 : 2;
-        return ng == 4 ? DecodePlan{4, 4, 2, s} : DecodePlan{2, 8, 1, s};
+        if (ng == 2) return DecodePlan{2, 8, 1, s};
+        // 48-column strips where they fill the CUs better (qkv at batch 64,
+        // two K slices: 256 workgroups instead of 192, 23.0 -> 20.6 us)
+        return DecodePlan{M > 32 && s == 2 ? fill_ng(N, 2, {3, 4}) : 4, 4, 2, s};
     }
     // NVFP4 and fused: the same plan, so both sum in the same order
     if (M <= 16) return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 16, 1, 1};
     if (K >= 8192) return {4, 8, 1, 4, false};
-    // wide layers at batch 33-64: 32-column strips of 4 waves, two chunks per
-    // stage (gate_up at batch 64: 42.9 us against 47.2 with 64-column strips)
-    if (N >= 16384 && M > 32) return {2, 4, 2, 1};
+    // wide layers at batch 33-64: 4 waves, strips that fill whole rounds of
+    // the CUs (gate_up at batch 64 on decode-packed weights: 96-column strips,
+    // 256 workgroups, 25.7 us against 36.0 with 32-column strips of 768)
+    if (N >= 16384 && M > 32) return {fill_ng(N, 1, {4, 6, 8}), 4, 1, 1};
     return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 8, 2, 1};
 }
 
@@ -788,6 +814,10 @@ hipError_t launch_bf16_mg(const uint16_t *a, const uint16_t *w, int64_t M, int64
                           int out_type, int64_t ld_out, const DecodePlan &p, int S, float *part, hipStream_t s,
                           int pk) {
     if (p.ng == 8) return launch_bf16_cfg<MG, 8, 4, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    if constexpr (MG == 4) {
+        if (p.ng == 6) return launch_bf16_cfg<4, 6, 4, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+        if (p.ng == 3) return launch_bf16_cfg<4, 3, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
+    }
     if (p.ng == 4) return launch_bf16_cfg<MG, 4, 4, 2>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if (p.ng == 2 && p.waves == 8) return launch_bf16_cfg<MG, 2, 8, 1>(a, w, M, N, K, out, out_type, ld_out, S, part, s, pk);
     if constexpr (MG == 1)
@@ -825,14 +855,21 @@ hipError_t launch_nv_mg(const uint8_t *ac, const uint8_t *as, const float *aa_in
         if (decode_fp4_form(M, K))
             return launch_f4<A_NVFP4>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, p, S, part, s, nullptr, 0,
                                       pk);
+    if constexpr (MG == 4)
+        if (p.waves == 4) {  // wide layers at batch 33-64
+            if (p.ng == 4)
+                return launch_nvfp4_cfg<4, 4, 4, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                    nullptr, 0, pk);
+            if (p.ng == 6)
+                return launch_nvfp4_cfg<4, 6, 4, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                    nullptr, 0, pk);
+            return launch_nvfp4_cfg<4, 8, 4, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
+                                                nullptr, 0, pk);
+        }
     if (p.ng == 4 && !p.pipe)
         return launch_nvfp4_cfg<MG, 4, 8, 1, A_NVFP4, false, false>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type,
                                                                     ld_out, S, part, s, nullptr, 0, pk);
     if (p.ng == 4) return launch_nvfp4_cfg<MG, 4, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
-                                                       nullptr, 0, pk);
-    if constexpr (MG == 4)
-        if (p.ng == 2 && p.waves == 4)
-            return launch_nvfp4_cfg<4, 2, 4, 2>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
                                                        nullptr, 0, pk);
     if (p.ng == 2) return launch_nvfp4_cfg<MG, 2, 8, 1>(ac, as, aa, wc, ws, wa, M, N, K, out, out_type, ld_out, S, part, s,
                                                        nullptr, 0, pk);
