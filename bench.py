@@ -588,7 +588,7 @@ def _decode(nv, wl, layers, s, e):
                            device=dev)) for L in layers]
         # the library's route (include/nvfp4.h, nvfp4_quant_gemm): which layers quantize in the decode kernel
         fused = [L["K"] % 32 == 0 and Md * L["K"] <= 196608 and
-                 (Md <= 2 or (Md <= 8 and L["N"] <= 8192 and Md * L["K"] <= 32768)) for L in layers]
+                 (Md <= 2 or (Md <= 6 and L["N"] <= 8192 and Md * L["K"] <= 32768)) for L in layers]
 
         def dec4_step(c):
             for i, L in enumerate(layers):

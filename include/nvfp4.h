@@ -194,14 +194,16 @@ size_t nvfp4_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   exit); dynamic alpha needs at least nvfp4_quantize_workspace_size(M, K)
  *   bytes (NVFP4_EWORKSPACE otherwise).
  * Paths, by shape and workspace:
- *   - K % 32 == 0 and either M <= 2 with M * K <= 196608, or M <= 8 with
+ *   - K % 32 == 0 and either M <= 2 with M * K <= 196608, or M <= 6 with
  *     N <= 8192 and M * K <= 32768: one decode kernel quantizes the batch
  *     into LDS in every workgroup (each forms the dynamic alpha itself) and
  *     streams the weights (larger batches, and wider layers, measured faster
  *     quantized once);
  *   - otherwise, with nvfp4_quant_gemm_workspace_size(M, N, K) bytes: the
  *     quantizer writes codes and scales into the workspace and nvfp4_gemm's
- *     kernels run on them (one quantization per activation element; the
+ *     kernels run on them (decode batches of 3-64 rows with K % 128 == 0 in
+ *     the decode kernel's block layout of nvfp4_decode_pack, so each of its
+ *     loads reads 1 KB contiguous; one quantization per activation element; the
  *     in-prologue variant below repeats it for every column tile and measured
  *     slower at every prefill size);
  *   - otherwise: a tile kernel quantizes the activations in its operand

@@ -51,17 +51,30 @@ int check_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *alpha,
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+bool decode_shape(int64_t M, int64_t K, int kmult) {
+    return M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % kmult == 0;
+}
+
 // nvfp4_quant_gemm's workspace when it quantizes into the workspace and then
-// runs the NVFP4 GEMM: codes [M, K/2], scales [M, K/16], the amax partials
-// (dynamic alpha) and the GEMM's split-K partials, each 256-byte aligned.
+// runs the NVFP4 GEMM: codes [M, K/2], scales [M, K/16] (or, for the decode
+// kernel's batches of more than two rows with K % 128 == 0, both in its
+// packed block layout at `codes`), the amax partials (dynamic alpha) and the
+// GEMM's split-K partials, each 256-byte aligned.
 struct QgLayout {
     size_t codes, scales, parts, split, total;
+    bool pack_a;
 };
 QgLayout qg_layout(int64_t M, int64_t N, int64_t K, bool dyn) {
     QgLayout l;
     l.codes = 0;
-    l.scales = align256((size_t)M * (size_t)(K / 2));
-    l.parts = l.scales + align256((size_t)M * (size_t)(K / 16));
+    l.pack_a = decode_shape(M, K, 32) && nvfp4::decode_pack_a_route(M, K);
+    if (l.pack_a) {
+        l.scales = align256(nvfp4::decode_pack_a_bytes(M, K));
+        l.parts = l.scales;
+    } else {
+        l.scales = align256((size_t)M * (size_t)(K / 2));
+        l.parts = l.scales + align256((size_t)M * (size_t)(K / 16));
+    }
     l.split = l.parts + (dyn ? align256((size_t)nvfp4::amax_parts(M, K) * sizeof(uint32_t)) : 0);
     size_t split_bytes = 0;
     if (M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % 32 == 0)
@@ -72,9 +85,6 @@ QgLayout qg_layout(int64_t M, int64_t N, int64_t K, bool dyn) {
 
 bool fused_decode_shape(int64_t M, int64_t N, int64_t K) { return nvfp4::fused_decode_route(M, N, K); }
 
-bool decode_shape(int64_t M, int64_t K, int kmult) {
-    return M <= nvfp4::kSkinnyMaxM && K < nvfp4::kSkinnyMaxK && K % kmult == 0;
-}
 
 int quantize_impl(const char *fn, const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
                   uint8_t *scales, float *alpha, int alpha_mode, void *workspace, size_t workspace_bytes,
@@ -292,15 +302,17 @@ int nvfp4_quant_gemm(const void *x_bf16, int64_t ld_x, float *a_alpha, int alpha
         uint8_t *codes = wsb + l.codes, *scales = wsb + l.scales;
         const int nparts = nvfp4::amax_parts(M, K);
         if ((rc = hip_status(dyn ? nvfp4::launch_quantize_dynamic((const uint16_t *)x_bf16, M, K, ld_x, codes, scales,
-                                                                  a_alpha, (uint32_t *)(wsb + l.parts), nparts, s)
+                                                                  a_alpha, (uint32_t *)(wsb + l.parts), nparts, s,
+                                                                  l.pack_a)
                                  : nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha,
-                                                          0, nullptr, nparts, s),
+                                                          0, nullptr, nparts, s, l.pack_a),
                              "quantize kernel")))
             return rc;
         if (decode_shape(M, K, 32))
             return hip_status(nvfp4::launch_skinny_nvfp4(codes, scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K,
                                                          out, out_dtype, ld_out, wsb + l.split,
-                                                         workspace_bytes - l.split, s),
+                                                         workspace_bytes - l.split, s,
+                                                         l.pack_a ? nvfp4::kPackA : 0),
                               "nvfp4 decode kernel");
         return hip_status(nvfp4::launch_gemm_nvfp4(codes, scales, a_alpha, w_codes, w_scales, w_alpha, M, N, K, out,
                                                    out_dtype, ld_out, s),
@@ -480,13 +492,14 @@ int nvfp4_quant_gemm_packed(const void *x_bf16, int64_t ld_x, float *a_alpha, in
     uint8_t *codes = wsb + l.codes, *scales = wsb + l.scales;
     const int nparts = nvfp4::amax_parts(M, K);
     if ((rc = hip_status(dyn ? nvfp4::launch_quantize_dynamic((const uint16_t *)x_bf16, M, K, ld_x, codes, scales,
-                                                              a_alpha, (uint32_t *)(wsb + l.parts), nparts, s)
+                                                              a_alpha, (uint32_t *)(wsb + l.parts), nparts, s, l.pack_a)
                              : nvfp4::launch_quantize((const uint16_t *)x_bf16, M, K, ld_x, codes, scales, a_alpha, 0,
-                                                      nullptr, nparts, s),
+                                                      nullptr, nparts, s, l.pack_a),
                          "quantize kernel")))
         return rc;
     return hip_status(nvfp4::launch_skinny_nvfp4(codes, scales, a_alpha, w_packed, nullptr, w_alpha, M, N, K, out,
-                                                 out_dtype, ld_out, wsb + l.split, workspace_bytes - l.split, s, true),
+                                                 out_dtype, ld_out, wsb + l.split, workspace_bytes - l.split, s,
+                                                 nvfp4::kPackW | (l.pack_a ? nvfp4::kPackA : 0)),
                       "nvfp4 decode kernel");
 }
 

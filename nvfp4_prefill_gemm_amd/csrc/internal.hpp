@@ -37,15 +37,19 @@ bool quantize_self_amax(int64_t rows, int64_t cols);
 
 // dynamic != 0: alpha = amax / 2688 is written to *alpha, the amax taken from
 // partials[0..nparts), or from the tensor itself when quantize_self_amax().
+// pack_a: codes and scales go to `codes` in the decode kernel's packed block
+// layout (decode_pack_a_bytes(rows, cols) bytes, cols % 128 == 0; rows of the
+// last group past `rows` are left unwritten; `scales` unused).
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials,
-                           int nparts, hipStream_t s);
+                           int nparts, hipStream_t s, bool pack_a = false);
 
 // Dynamic-alpha quantization: the single launch of quantize_self_amax()
 // tensors, else the amax pass into partials (amax_parts(rows, cols) = nparts
 // entries) and the quantize pass.
 hipError_t launch_quantize_dynamic(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
-                                   uint8_t *scales, float *alpha, uint32_t *partials, int nparts, hipStream_t s);
+                                   uint8_t *scales, float *alpha, uint32_t *partials, int nparts, hipStream_t s,
+                                   bool pack_a = false);
 
 // Device address and size of this device's scratch array for the amax
 // partials of nvfp4_quantize_noalloc (looked up once per device).
@@ -131,12 +135,23 @@ hipError_t launch_decode_pack(const uint8_t *w_codes, const uint8_t *w_scales, i
 
 // NVFP4 x NVFP4 at decode shapes: M <= kSkinnyMaxM, K % 32 == 0, codes
 // 16-byte and scales 2-byte aligned (nvfp4_gemm checks and otherwise uses the
-// tile kernel).  packed: w_codes is the decode-packed weight (w_scales
-// unused, K % 128 == 0).
+// tile kernel).  packed: kPackW, w_codes is the decode-packed weight
+// (w_scales unused, K % 128 == 0); kPackA, a_codes holds the activation in
+// the same block layout (a_scales unused; K % 128 == 0 and not the FP4-MFMA
+// form, i.e. M > 2), as launch_quantize writes it with pack_a.
+constexpr int kPackW = 1, kPackA = 2;
 hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                                int64_t M, int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
-                               size_t ws_bytes, hipStream_t s, bool packed = false);
+                               size_t ws_bytes, hipStream_t s, int packed = 0);
+// Activation batches that nvfp4_quant_gemm quantizes into its workspace in
+// the packed block layout for the decode kernel.
+inline bool decode_pack_a_route(int64_t M, int64_t K) { return M > 2 && M <= 64 && K % 128 == 0; }
+// Bytes of an [M, K] activation in that layout: one kPackBlock block per 16
+// rows (the last group padded) and 128-wide chunk.
+inline size_t decode_pack_a_bytes(int64_t M, int64_t K) {
+    return (size_t)((M + 15) / 16) * (size_t)(K / 128) * (size_t)kPackBlock;
+}
 
 // Fused decode (BF16 activations quantized into LDS by every workgroup):
 // M <= 16, M * K <= kFusedDecodeMaxElems, K % 32 == 0, x rows 16-byte
@@ -152,11 +167,12 @@ hipError_t launch_skinny_fused(const uint16_t *x, int64_t ld_x, float *a_alpha, 
 // most kFusedDecodeWideM rows on layers of at most kFusedDecodeWideN
 // columns whose batch fits a workgroup's registers (M * K <=
 // kFusedDecodeRegElems): there the per-workgroup quantization costs less
-// than a separate quantizer launch (measured at batch 4 and 8 on the
-// Qwen3-8B qkv and o projections), while wide layers repeat it too often.
+// than a separate quantizer launch (measured at batch 3-6 on the Qwen3-8B
+// qkv and o projections; at batch 8 quantizing once into the packed block
+// layout is faster), while wide layers repeat it too often.
 constexpr int64_t kFusedDecodeMaxM = 2;
 constexpr int64_t kFusedDecodeMaxElems = 16 * 12288;
-constexpr int64_t kFusedDecodeWideM = 8;
+constexpr int64_t kFusedDecodeWideM = 6;
 constexpr int64_t kFusedDecodeWideN = 8192;
 constexpr int64_t kFusedDecodeRegElems = 32768;
 inline bool fused_decode_route(int64_t M, int64_t N, int64_t K) {

@@ -158,6 +158,7 @@ struct QItems {
     uint8_t *codes, *scales;
     int64_t cols, ld;
     uint32_t nseg, items, lane;
+    uint32_t pk_bytes;  // kPk: bytes of the packed activation at `codes`
 
     __device__ __forceinline__ void load(uint32_t it, uint4 *v) const {
         const bool ok = it < items;
@@ -171,11 +172,17 @@ struct QItems {
     }
 
     // Eq. 3 against t = alpha * 6 (rt = RN(1/t)), Eq. 2 through the divisor
-    // table, codes and scale bytes stored
+    // table, codes and scale bytes stored: row-major, or (kPk) in the decode
+    // kernel's block layout, where block (r / 16, el / 128) holds the 8 code
+    // bytes of elements el .. el + 15 of row r at 16 l + (el % 32) / 2 with
+    // l = r % 16 + 16 ((el % 128) / 32) (the bytes decode lane l loads), and
+    // their scale at 1024 + 8 (r % 16) + (el % 128) / 16
+    template <bool kPk>
     __device__ __forceinline__ void quant(uint32_t it, const uint4 *v, float t, float rt, const float4 *dtab) const {
         const bool ok = it < items;
         const uint32_t r = ok ? it / nseg : 0u, e0 = (it - r * nseg) * (kSeg * 8) + lane * 16u;
-        const rsrc_t cs = make_rsrc(codes + (int64_t)r * (cols >> 1), ok ? (uint32_t)(cols >> 1) : 0u);
+        const rsrc_t cs = kPk ? make_rsrc(codes, pk_bytes)
+                              : make_rsrc(codes + (int64_t)r * (cols >> 1), ok ? (uint32_t)(cols >> 1) : 0u);
         const rsrc_t ss = make_rsrc(scales + (int64_t)r * (cols >> 4), ok ? (uint32_t)(cols >> 4) : 0u);
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
@@ -196,8 +203,17 @@ struct QItems {
                 lo = quant8(w, e.x);
                 hi = quant8(w + 4, e.x);
             }
-            buf_store8(lo, hi, cs, el >> 1);
-            buf_store1(code, ss, el >> 4);
+            if constexpr (kPk) {
+                const uint32_t blk = ((r >> 4) * (uint32_t)(cols >> 7) + (el >> 7)) * (uint32_t)kPackBlock;
+                const bool in = ok & (el < (uint32_t)cols);
+                const uint32_t co = blk + 16u * ((r & 15u) + 16u * ((el & 127u) >> 5)) + ((el & 31u) >> 1);
+                const uint32_t so = blk + 1024u + 8u * (r & 15u) + ((el & 127u) >> 4);
+                buf_store8(lo, hi, cs, in ? co : kBufOOB);
+                buf_store1(code, cs, in ? so : kBufOOB);
+            } else {
+                buf_store8(lo, hi, cs, el >> 1);
+                buf_store1(code, ss, el >> 4);
+            }
         }
     }
 };
@@ -214,18 +230,19 @@ __device__ __forceinline__ void fill_dtab(float4 *dtab, float alpha) {
     }
 }
 
-template <int kAlpha>
+template <int kAlpha, bool kPk = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ld, uint8_t *__restrict__ codes,
                                                             uint8_t *__restrict__ scales, float *__restrict__ alpha_io,
-                                                            const uint32_t *__restrict__ partials, int nparts) {
+                                                            const uint32_t *__restrict__ partials, int nparts,
+                                                            uint32_t pk_bytes) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // 32-bit item arithmetic: the host guarantees items < 2^31 and cols < 2^30
     const uint32_t octs = (uint32_t)(cols >> 3);  // 8-element groups per row; even, so pairs never straddle rows
     const uint32_t nseg = (octs + kSeg - 1) / kSeg;
     const uint32_t items = (uint32_t)rows * nseg, nw = gridDim.x * kWaves;
-    const QItems qi{x, codes, scales, cols, ld, nseg, items, lane};
+    const QItems qi{x, codes, scales, cols, ld, nseg, items, lane, pk_bytes};
     uint32_t it = blockIdx.x * kWaves + wave;
     // the tensor scale's inputs are read first, then the first item's loads
     // are issued, so waiting for the former leaves the latter in flight
@@ -264,11 +281,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t *__re
     // one is quantized
     for (;;) {
         qi.load(it + nw, vb);
-        qi.quant(it, va, t, rt, dtab);
+        qi.quant<kPk>(it, va, t, rt, dtab);
         it += nw;
         if (it >= items) break;
         qi.load(it + nw, va);
-        qi.quant(it, vb, t, rt, dtab);
+        qi.quant<kPk>(it, vb, t, rt, dtab);
         it += nw;
         if (it >= items) break;
     }
@@ -347,27 +364,46 @@ hipError_t launch_amax_partials(const uint16_t *x, int64_t rows, int64_t cols, i
 bool quantize_self_amax(int64_t rows, int64_t cols) { return rows * cols <= kSelfAmaxMaxElems; }
 
 hipError_t launch_quantize_dynamic(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
-                                   uint8_t *scales, float *alpha, uint32_t *partials, int nparts, hipStream_t s) {
+                                   uint8_t *scales, float *alpha, uint32_t *partials, int nparts, hipStream_t s,
+                                   bool pack_a) {
     if (quant_items(rows, cols) >= (int64_t(1) << 31) || cols >= (int64_t(1) << 30)) return hipErrorInvalidValue;
     if (!quantize_self_amax(rows, cols))
         if (hipError_t e = launch_amax_partials(x, rows, cols, ld, partials, nparts, s); e != hipSuccess) return e;
-    return launch_quantize(x, rows, cols, ld, codes, scales, alpha, 1, partials, nparts, s);
+    return launch_quantize(x, rows, cols, ld, codes, scales, alpha, 1, partials, nparts, s, pack_a);
 }
+
+namespace {
+
+template <bool kPk>
+void launch_quantize_kind(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes, uint8_t *scales,
+                          float *alpha, int dynamic, const uint32_t *partials, int nparts, hipStream_t s,
+                          uint32_t pk_bytes) {
+    const dim3 block(kThreads);
+    if (dynamic && quantize_self_amax(rows, cols))
+        hipLaunchKernelGGL((quantize_kernel<ALPHA_SELF, kPk>), dim3(quant_grid<ALPHA_SELF>(rows, cols)), block, 0, s,
+                           x, rows, cols, ld, codes, scales, alpha, partials, nparts, pk_bytes);
+    else if (dynamic)
+        hipLaunchKernelGGL((quantize_kernel<ALPHA_PARTIALS, kPk>), dim3(quant_grid<ALPHA_PARTIALS>(rows, cols)), block,
+                           0, s, x, rows, cols, ld, codes, scales, alpha, partials, nparts, pk_bytes);
+    else
+        hipLaunchKernelGGL((quantize_kernel<ALPHA_STATIC, kPk>), dim3(quant_grid<ALPHA_STATIC>(rows, cols)), block, 0,
+                           s, x, rows, cols, ld, codes, scales, alpha, partials, nparts, pk_bytes);
+}
+
+}  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint8_t *scales, float *alpha, int dynamic, const uint32_t *partials, int nparts,
-                           hipStream_t s) {
+                           hipStream_t s, bool pack_a) {
     if (quant_items(rows, cols) >= (int64_t(1) << 31) || cols >= (int64_t(1) << 30)) return hipErrorInvalidValue;
-    const dim3 block(kThreads);
-    if (dynamic && quantize_self_amax(rows, cols))
-        hipLaunchKernelGGL(quantize_kernel<ALPHA_SELF>, dim3(quant_grid<ALPHA_SELF>(rows, cols)), block, 0, s, x, rows,
-                           cols, ld, codes, scales, alpha, partials, nparts);
-    else if (dynamic)
-        hipLaunchKernelGGL(quantize_kernel<ALPHA_PARTIALS>, dim3(quant_grid<ALPHA_PARTIALS>(rows, cols)), block, 0, s,
-                           x, rows, cols, ld, codes, scales, alpha, partials, nparts);
-    else
-        hipLaunchKernelGGL(quantize_kernel<ALPHA_STATIC>, dim3(quant_grid<ALPHA_STATIC>(rows, cols)), block, 0, s, x,
-                           rows, cols, ld, codes, scales, alpha, partials, nparts);
+    if (pack_a) {
+        const size_t pk = decode_pack_a_bytes(rows, cols);
+        if (cols % 128 != 0 || pk >= (size_t(1) << 31)) return hipErrorInvalidValue;
+        launch_quantize_kind<true>(x, rows, cols, ld, codes, scales, alpha, dynamic, partials, nparts, s,
+                                   (uint32_t)pk);
+    } else {
+        launch_quantize_kind<false>(x, rows, cols, ld, codes, scales, alpha, dynamic, partials, nparts, s, 0u);
+    }
     return hipGetLastError();
 }
 

@@ -264,24 +264,31 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     // row-major codes [N, K/2] and scales [N, K/16] (steps 64 and 8), or the
     // decode-packed blocks (one 1152-byte block per 16 rows and chunk, both
     // steps 1152; rows past N are zeros in the last group's blocks).
+    // The activation codes may come in the same packed layout (kPackA: made
+    // by the quantizer for nvfp4_quant_gemm's quantize-first batches, A_NVFP4
+    // without the FP4-MFMA form): then a row group's chunk is one block too.
+    const bool wpk = packed & kPackW, apk = packed & kPackA;
     const int64_t nrows = N - n0 < NG * 16 ? N - n0 : NG * 16;
     const int64_t nchunks = K >> 7, gbytes = nchunks * kPackBlock;  // packed bytes per 16-row group
     const int64_t ngroups = (nrows + 15) >> 4;
-    const rsrc_t wcs = packed ? make_rsrc(wc + (n0 >> 4) * gbytes, (uint32_t)(ngroups * gbytes))
-                              : make_rsrc(wc + n0 * cb, (uint32_t)(nrows * cb));
-    const rsrc_t wss = packed ? wcs : make_rsrc(ws + n0 * sb, (uint32_t)(nrows * sb));
-    const uint32_t cstep = packed ? (uint32_t)kPackBlock : 64u, sstep = packed ? (uint32_t)kPackBlock : 8u;
-    const rsrc_t xcs = make_rsrc(ac, (uint32_t)(M * cb));
-    const rsrc_t xss = make_rsrc(as, (uint32_t)(M * sb));
+    const rsrc_t wcs = wpk ? make_rsrc(wc + (n0 >> 4) * gbytes, (uint32_t)(ngroups * gbytes))
+                           : make_rsrc(wc + n0 * cb, (uint32_t)(nrows * cb));
+    const rsrc_t wss = wpk ? wcs : make_rsrc(ws + n0 * sb, (uint32_t)(nrows * sb));
+    const uint32_t cstep = wpk ? (uint32_t)kPackBlock : 64u, sstep = wpk ? (uint32_t)kPackBlock : 8u;
+    const rsrc_t xcs = apk ? make_rsrc(ac, (uint32_t)(((M + 15) >> 4) * gbytes)) : make_rsrc(ac, (uint32_t)(M * cb));
+    const rsrc_t xss = apk ? xcs : make_rsrc(as, (uint32_t)(M * sb));
     uint32_t wco[NG], wso[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         const int r = j * 16 + (lane & 15);
-        wco[j] = packed ? (uint32_t)(j * gbytes + lane * 16) : (uint32_t)(r * cb + (lane >> 4) * 16);
-        wso[j] = packed ? (uint32_t)(j * gbytes + 1024 + (lane & 15) * 8 + (lane >> 4) * 2)
-                        : (uint32_t)(r * sb + (lane >> 4) * 2);
+        wco[j] = wpk ? (uint32_t)(j * gbytes + lane * 16) : (uint32_t)(r * cb + (lane >> 4) * 16);
+        wso[j] = wpk ? (uint32_t)(j * gbytes + 1024 + (lane & 15) * 8 + (lane >> 4) * 2)
+                     : (uint32_t)(r * sb + (lane >> 4) * 2);
     }
-    uint32_t xco[MG], xso[MG];
+    // A offsets of chunk 0 (row-major: the row's start; the lane's K part
+    // and the chunk are added per load) and, packed, the lane's bytes of
+    // chunk 0 in its row group's blocks (+ kPackBlock per chunk)
+    uint32_t xco[MG], xso[MG], xpo[MG];
     bool xv[MG];
 #pragma unroll
     for (int i = 0; i < MG; ++i) {
@@ -289,7 +296,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
         xv[i] = m < M;
         xco[i] = (uint32_t)((xv[i] ? m : 0) * cb);
         xso[i] = (uint32_t)((xv[i] ? m : 0) * sb);
+        xpo[i] = (uint32_t)(i * gbytes + lane * 16);
     }
+    const uint32_t xps = 1024u + (uint32_t)((lane & 15) * 8 + (lane >> 4) * 2) - (uint32_t)(lane * 16);  // code -> scale
     // kF4: this lane's A-operand piece (8 code bytes of block fr % 8 of batch
     // row fr / 8, in half fr % 2 of the lane's 32 K, when that block lies in
     // the lane's K range) and its output rows' scale words (4 bytes: blocks
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
     uint32_t f_wso[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j)
-        f_wso[j] = packed ? (uint32_t)(j * gbytes + 1024 + (lane & 15) * 8 + 4 * (fg & 1))
+        f_wso[j] = wpk ? (uint32_t)(j * gbytes + 1024 + (lane & 15) * 8 + 4 * (fg & 1))
                           : (uint32_t)((j * 16 + (lane & 15)) * sb + 4 * (fg & 1));
     const uint8_t *lc = nullptr, *ls = nullptr;  // LDS copy of A (fused path)
     float alpha_a = 0.0f;
@@ -353,8 +362,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_nvfp4_kernel(
 #pragma unroll
             for (int i = 0; i < MG; ++i) {
                 if constexpr (kA == A_NVFP4) {
-                    st.xq[u][i] = buf_load16(xcs, (kin & xv[i]) ? xco[i] + kc : kBufOOB);
-                    st.xsc[u][i] = buf_load2(xss, (kin & xv[i]) ? xso[i] + ksc : kBufOOB);
+                    const uint32_t pc = xpo[i] + (uint32_t)c * (uint32_t)kPackBlock;
+                    st.xq[u][i] = buf_load16(xcs, (kin & xv[i]) ? (apk ? pc : xco[i] + kc) : kBufOOB);
+                    st.xsc[u][i] = buf_load2(xss, (kin & xv[i]) ? (apk ? pc + xps : xso[i] + ksc) : kBufOOB);
                 } else {  // LDS: clamp the address, zero by select
                     const uint32_t kk = kin ? kc : 0u, kks = kin ? ksc : 0u;
                     const uint4 q = *reinterpret_cast<const uint4 *>(lc + xco[i] + kk);
@@ -910,7 +920,8 @@ hipError_t launch_skinny_bf16(const uint16_t *a, const uint16_t *w, int64_t M, i
 hipError_t launch_skinny_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
                                const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha, int64_t M,
                                int64_t N, int64_t K, void *out, int out_type, int64_t ld_out, void *ws,
-                               size_t ws_bytes, hipStream_t s, bool packed) {
+                               size_t ws_bytes, hipStream_t s, int packed) {
+    if ((packed & kPackA) && (decode_fp4_form(M, K) || K % 128 != 0)) return hipErrorInvalidValue;
     const DecodePlan p = decode_plan(DECODE_NVFP4, M, N, K);
     const int S = plan_slices(p, M, N, ws, ws_bytes);
     float *part = (float *)ws;

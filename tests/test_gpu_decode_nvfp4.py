@@ -137,13 +137,15 @@ def test_decode_kernel_agrees_with_tile_kernel(nv, oracle_mod):
                                           (2, 24576, 4096, 16),
                                           # two 16-row weight groups per workgroup, the last one partial
                                           (3, 6200, 1056, 0), (1, 16400, 512, 8), (2, 6200, 12288, 0),
-                                          # batch 3-8 on layers up to 8192 columns with M * K <= 32768
-                                          # (in-kernel), and just past each limit (quantized once)
-                                          (8, 6144, 4096, 0), (4, 4096, 4096, 8), (5, 8192, 4096, 0),
-                                          (8, 8200, 4096, 0), (6, 520, 5472, 0), (8, 4096, 4128, 0)])
+                                          # batch 3-6 on layers up to 8192 columns with M * K <= 32768
+                                          # (in-kernel), and just past each limit (quantized once,
+                                          # into the packed block layout when K % 128 == 0)
+                                          (6, 6144, 4096, 0), (4, 4096, 4096, 8), (5, 8192, 4096, 0),
+                                          (6, 8200, 4096, 0), (6, 520, 5472, 0), (6, 4096, 4128, 0),
+                                          (7, 6144, 4096, 0), (8, 6144, 4096, 0), (8, 4096, 4096, 8)])
 def test_fused_decode_equals_quantize_then_gemm(nv, oracle_mod, M, N, K, ld_pad):
     """nvfp4_quant_gemm at decode sizes: M <= 2 with M * K <= 196608, and
-    M <= 8 with N <= 8192 and M * K <= 32768, quantize the batch inside the
+    M <= 6 with N <= 8192 and M * K <= 32768, quantize the batch inside the
     decode kernel (the batch held in registers when it fits, else read
     twice); other batches quantize once into the workspace.  Either way
     alpha, and the output in FP32 and BF16, equal nvfp4_quantize followed by

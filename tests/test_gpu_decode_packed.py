@@ -99,6 +99,44 @@ def test_quant_gemm_packed_equals_row_major(nv, oracle_mod, M, N, K):
         assert torch.equal(y_st, y_rm)
 
 
+@pytest.mark.parametrize("M,N,K,ld_pad", [(3, 1000, 128, 0), (7, 6144, 4096, 8), (8, 24576, 4096, 0),
+                                          (17, 520, 1152, 0), (33, 6144, 4096, 16), (40, 4096, 12288, 0),
+                                          (63, 24576, 4096, 0), (64, 4100, 12288, 8), (64, 16, 128, 0)])
+def test_quant_gemm_packed_activation_layout(nv, oracle_mod, M, N, K, ld_pad):
+    """Decode batches of 3-64 rows with K % 128 == 0 that nvfp4_quant_gemm
+    quantizes into its workspace: the quantizer writes the batch in the decode
+    kernel's block layout (ragged last row group, strided x).  Row-major and
+    packed weights, dynamic and static alpha, FP32 and BF16 out: equal bit for
+    bit to nvfp4_quantize followed by nvfp4_gemm (row-major codes), and within
+    the gate of the oracle's exact product."""
+    import torch
+
+    g = np.random.default_rng(M * 31 + N * 5 + K)
+    a = wl.activations(M, K, g)
+    wt = wl.weights(N, K, g)
+    A, W = oracle_mod.quantize(a), oracle_mod.quantize(wt)
+    wc, wsc, wal = u8_dev(W[0]), u8_dev(W[1]), f32_dev([W[2]])
+    wp = nv.nvfp4_decode_pack(wc, wsc, wal)
+    xfull = torch.zeros((M, K + ld_pad), dtype=torch.bfloat16, device="cuda")
+    xfull[:, :K] = bf16_dev(a)
+    x = xfull[:, :K]
+    say("quant gemm packed activation", M, N, K, ld_pad)
+    ac, asc, aal = nv.nvfp4_quantize(x)
+    assert host(aal)[0] == A[2]
+    for od in (torch.float32, torch.bfloat16):
+        y_ref = nv.nvfp4_gemm(ac, asc, aal, wc, wsc, wal, out_dtype=od)
+        y_rm, al_rm = nv.nvfp4_quant_gemm(x, wc, wsc, wal, out_dtype=od)
+        y_pk, al_pk = nv.nvfp4_quant_gemm_packed(x, wp, out_dtype=od)
+        assert host(al_rm)[0] == host(al_pk)[0] == A[2]
+        assert torch.equal(y_rm, y_ref), f"quant_gemm differs from quantize + gemm ({od})"
+        assert torch.equal(y_pk, y_ref), f"quant_gemm_packed differs from quantize + gemm ({od})"
+        y_st, _ = nv.nvfp4_quant_gemm_packed(x, wp, a_alpha=f32_dev([A[2]]), static_alpha=True, out_dtype=od)
+        assert torch.equal(y_st, y_ref)
+        tol = parity.GEMM_TOL_F32 if od == torch.float32 else parity.GEMM_TOL_BF16
+        parity.assert_gemm_close(y_pk.float().cpu().numpy(), oracle_mod.gemm_exact(*A, *W), tol,
+                                 f"packed activation {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M", wl.PHASE_SPLIT_DECODE_M)
 def test_quant_gemm_packed_qwen3_8b_vs_oracle(nv, oracle_mod, M):
     """Batch 1/8/64 through the Qwen3-8B qkv and down projections on packed
