@@ -798,12 +798,18 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
     }
     // NVFP4 and fused: the same plan, so both sum in the same order
     if (M <= 16) return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 16, 1, 1};
-    if (K >= 8192) return {4, 8, 1, 4, false};
+    // batch 33-64 with the activation in the packed block layout (the
+    // quantize-first route of nvfp4_quant_gemm): narrow and long-K layers
+    // take one 16-column group of 16 waves, unsplit (down at batch 64 on
+    // decode-packed weights 26.4 -> 23.8 us against 4 groups over 4 K
+    // slices, o 15.4 -> 14.9 us against 8 waves of two chunks per stage)
+    if (K >= 8192) return M > 32 ? DecodePlan{1, 16, 1, 1} : DecodePlan{4, 8, 1, 4, false};
     // wide layers at batch 33-64: 4 waves, strips that fill whole rounds of
     // the CUs (gate_up at batch 64 on decode-packed weights: 96-column strips,
     // 256 workgroups, 25.7 us against 36.0 with 32-column strips of 768)
     if (N >= 16384 && M > 32) return {fill_ng(N, 1, {4, 6, 8}), 4, 1, 1};
-    return N >= 6144 ? DecodePlan{2, 8, 1, 1} : DecodePlan{1, 8, 2, 1};
+    if (N >= 6144) return {2, 8, 1, 1};
+    return M > 32 ? DecodePlan{1, 16, 1, 1} : DecodePlan{1, 8, 2, 1};
 }
 
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
