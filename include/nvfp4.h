@@ -72,7 +72,7 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 /*
  * BF16 -> NVFP4 quantization (Mix-Quant Section 3.3, Eq. 3 then Eq. 2).
  * Dynamic alpha: an amax pass writes per-workgroup partial maxima to the
- * workspace, then the quantize pass runs; a tensor of at most 32768
+ * workspace, then the quantize pass runs; a tensor of at most 65536
  * elements (a decode batch) takes one launch, every workgroup forming the
  * amax itself, and leaves the workspace untouched.
  *   x_bf16   [rows, ld_x] BF16, 16-byte aligned, ld_x % 8 == 0

@@ -116,35 +116,40 @@ __global__ __launch_bounds__(kThreads) void alpha_kernel(const uint32_t *__restr
 // amax pass's partials, or the workgroup's own pass over a small tensor.
 enum AlphaSrc { ALPHA_STATIC = 0, ALPHA_PARTIALS = 1, ALPHA_SELF = 2 };
 
-// Max |x| over a whole small tensor (at most kSelfLoads * kThreads octets)
-// by one workgroup, as FP32 bits of the BF16 maximum: every workgroup of the
-// single-launch mode reads the tensor once, all its loads in flight together,
-// instead of waiting for a separate amax launch.  Slots past the tensor
-// load its first octet again (it is part of the tensor, so the maximum is
-// unchanged): the loads carry no condition and are all issued before the
-// first use, so they are in flight together.
+// Max |x| over a whole small tensor (at most kSelfRounds * kSelfLoads *
+// kThreads octets) by one workgroup, as FP32 bits of the BF16 maximum: every
+// workgroup of the single-launch mode reads the tensor once, in rounds of
+// kSelfLoads loads per thread that are all in flight together, instead of
+// waiting for a separate amax launch.  Slots past the tensor load its first
+// octet again (it is part of the tensor, so the maximum is unchanged): the
+// loads of a round carry no condition and are all issued before the first
+// use.  The round count is uniform across the workgroup.
 constexpr int kSelfLoads = 16;
+constexpr int kSelfRounds = 2;
 __device__ __forceinline__ uint32_t tensor_amax_bits(const uint16_t *__restrict__ x, uint32_t rows, uint32_t octs,
                                                      int64_t ld) {
     const uint32_t total = rows * octs;
-    uint4 v[kSelfLoads];
-#pragma unroll
-    for (int u = 0; u < kSelfLoads; ++u) {
-        const uint32_t o = threadIdx.x + u * kThreads, oc = o < total ? o : 0u, r = oc / octs;
-        v[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (oc - r * octs) * 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
     ushort2_t m = {0, 0};
+    for (uint32_t base = 0; base < total; base += kSelfLoads * kThreads) {
+        uint4 v[kSelfLoads];
 #pragma unroll
-    for (int u = 0; u < kSelfLoads; ++u) {
-        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
-        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
-        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
-        m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
+        for (int u = 0; u < kSelfLoads; ++u) {
+            const uint32_t o = base + threadIdx.x + u * kThreads, oc = o < total ? o : 0u, r = oc / octs;
+            v[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + (oc - r * octs) * 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the round issued before the first use
+#pragma unroll
+        for (int u = 0; u < kSelfLoads; ++u) {
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].x));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].y));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].z));
+            m = __builtin_elementwise_max(m, abs_bf16x2(v[u].w));
+        }
     }
     return max((uint32_t)m.x, (uint32_t)m.y) << 16;
 }
-static_assert(kSelfLoads * kThreads * 8 >= kSelfAmaxMaxElems, "the single-launch amax reads the whole tensor");
+static_assert(kSelfRounds * kSelfLoads * kThreads * 8 >= kSelfAmaxMaxElems,
+              "the single-launch amax reads the whole tensor in at most kSelfRounds rounds");
 
 // Work items of the quantize pass: item it is one wave's (row, segment) of
 // kSeg octets; lane l owns whole 16-element blocks, elements

@@ -187,12 +187,15 @@ def test_student_t_long_prefill_full_tensor(nv, oracle_mod):
 
 
 @pytest.mark.parametrize("rows,cols,ld_pad", [(8, 12288, 0), (32, 4096, 0), (33, 4096, 0), (17, 4112, 24),
-                                              (3, 40960, 8)])
+                                              (3, 40960, 8), (4, 8192, 0), (16, 4096, 0), (16, 4096, 8),
+                                              (15, 4368, 0), (3, 21856, 24), (64, 4096, 0)])
 def test_decode_batch_sizes_amax_placement(nv, oracle_mod, rows, cols, ld_pad):
-    """Decode-batch-sized tensors past the single-launch limit (amax pass +
-    quantize pass, few workgroups), strided rows: the largest magnitude placed
-    in the last row's tail, then in the first row, so every workgroup's
-    partial maximum must count."""
+    """Decode-batch-sized tensors on both sides of the single-launch limit
+    (at most 65536 elements: every workgroup reads the whole tensor in up to
+    two rounds of loads; above it the amax pass + quantize pass, few
+    workgroups), strided rows: the largest magnitude placed in the last row's
+    tail, then in the first row, so every round and every workgroup's partial
+    maximum must count."""
     g = np.random.default_rng(rows * 7 + cols)
     x = g.standard_normal((rows, cols), dtype=np.float32)
     for where in ((rows - 1, cols - 3), (0, 1)):
