@@ -48,7 +48,11 @@
 // the decode lanes load it, so each 16-byte-per-lane load instruction reads
 // 1 KB of consecutive bytes instead of 64 bytes from each of 16 rows.  Only
 // the weight offsets differ (a per-chunk stride), so both layouts give the
-// same results bit for bit.
+// same results bit for bit.  The NVFP4 activation of more than two rows can
+// come in the same block layout (16 batch rows per block, written so by the
+// quantizer for nvfp4_quant_gemm's quantize-first decode batches): the batch,
+// which every workgroup re-reads in full, then also moves 1 KB contiguous
+// per load instruction.
 #include <stdlib.h>
 #include <string.h>
 
