@@ -785,7 +785,10 @@ DecodePlan decode_plan(int kind, int64_t M, int64_t N, int64_t K) {
         // steps per stage (qkv on decode-packed weights, batch 1: 12.6 -> 11.1 us)
         if (M <= 16 && N >= 6144 && N < 16384) return {2, 4, 4, 1};
         if (M <= 4) return {1, 16, 1, 1, false};
-        if (M <= 16) return N >= 6144 ? DecodePlan{2, 16, 1, 1} : DecodePlan{1, 16, 1, 1, false};
+        // wide layers at batch 5-16: the same 32-column strips of 4 waves
+        // (gate_up at batch 8 on decode-packed weights, four-layer step
+        // 80.4 -> 78.8 us against 16 waves)
+        if (M <= 16) return N >= 6144 ? DecodePlan{2, 4, 4, 1} : DecodePlan{1, 16, 1, 1, false};
         // wide layers at batch 33-64: wide strips read the batch once per 64-128
         // columns (gate_up at batch 64: 77.9 -> 69.8 us with 128-column strips
         // instead of 64), and a width that fills whole rounds of the CUs
